@@ -1,0 +1,217 @@
+/*
+ * nvfp4moe.h -- C ABI of the MI355X (gfx950) NVFP4 MoE expert forward.
+ *
+ * The operation (sources: the miniTE summary page, "miniTE diagnoses and
+ * narrows the cross-engine execution gap of NVFP4 RL", sections "how it
+ * differs" and "how to use it"; the article "Finish RL training faster:
+ * bitwise consistent, high-performance, agent-driven", sections 4.4-4.6):
+ *
+ *   sort tokens by expert (device offsets mark each expert's rows) and take
+ *   the row amax in the same pass over X; pad each expert's rows; quantize
+ *   every row to NVFP4 -- E2M1 codes, one E4M3 scale per 16 elements, one
+ *   FP32 outer scale per row g = max|row| / (6*448), no Hadamard transform,
+ *   no stochastic rounding; grouped GEMM FC1 whose FP32 epilogue multiplies
+ *   by g^x * g^w and casts to BF16; h = SiLU(gate) * up * p (router
+ *   probability) in FP32 rounded once to BF16, and that producer also emits
+ *   the FC2 amax; quantize h; grouped GEMM FC2 with the same epilogue; sum
+ *   each token's K expert outputs in FP32 in top-k slot order, round to BF16.
+ *
+ * Every token's output is bitwise identical whatever else is in the batch:
+ * quantization is per row, each output row is accumulated in one fixed order
+ * with one instruction sequence for every batch size (no split-K, no
+ * configuration chosen by the token count), and the combine order is fixed.
+ *
+ * Conventions
+ *   - All pointers are DEVICE pointers unless marked (host).  BF16 tensors
+ *     are passed as uint16_t bit patterns, row-major.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued; nothing here synchronises except the calls marked "syncs".
+ *   - The library never allocates on the forward path: every buffer is the
+ *     caller's.  It keeps no mutable global state, so calls on different
+ *     streams with different workspaces are independent.
+ *   - Errors found on the host return before anything is launched.  No
+ *     exception crosses the ABI and nothing is printed.
+ *   - NaN or Inf inputs are outside the contract (results undefined).
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define NVFP4MOE_API __attribute__((visibility("default")))
+#else
+#define NVFP4MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+    NVFP4_OK = 0,
+    NVFP4_E_NULL = 1,      /* a required pointer is NULL */
+    NVFP4_E_SHAPE = 2,     /* a size is negative, too large, or not a multiple the layout needs */
+    NVFP4_E_ALIGN = 3,     /* a pointer is not aligned as documented */
+    NVFP4_E_WORKSPACE = 4, /* workspace_bytes smaller than the size function returned */
+    NVFP4_E_CAPACITY = 5,  /* T > cfg->max_tokens */
+    NVFP4_E_HIP = 6,       /* a HIP launch or runtime call failed */
+    NVFP4_E_MISMATCH = 7,  /* self-test found differing bits */
+    NVFP4_E_DEVICE = 8,    /* the device reported a contract violation (see nvfp4moe_device_error) */
+    NVFP4_E_ARG = 9        /* an enum argument is out of range */
+};
+
+/* Rounding of the E4M3 block scale v = amax_block / (6 g).  The pages fix the
+ * formats but not this rounding.  ROUND_UP (default) is the smallest E4M3
+ * value >= v, so scale * 6 * g always covers the block maximum; RNE rounds to
+ * the nearest E4M3 value (ties to an even mantissa).  Both clamp at 448. */
+enum { NVFP4_SCALE_RU = 0, NVFP4_SCALE_RNE = 1 };
+
+/* Layout of a quantized [rows, cols] matrix (three planes: codes, scales, g).
+ *
+ * LOGICAL: codes [rows][cols/2] bytes, element 2i in the low nibble of byte i;
+ *          scales [rows][cols/16] E4M3FN bytes; g [rows] FP32.
+ * GEMM:    the layout the grouped GEMM reads directly (rows % 32 == 0,
+ *          cols % 128 == 0).  Rows are grouped in tiles of 32, columns in
+ *          chunks of 64.  For row r (tile rt = r/32, rl = r%32) and column k
+ *          (chunk c = k/64, half h = (k%64)/32):
+ *            code byte  = (rt*(cols/64) + c)*1024 + (h*32 + rl)*16 + (k%32)/2,
+ *                         element k in the low nibble when k is even;
+ *            scale byte = (rt*(cols/128) + c/2)*256 + (h*32 + rl)*4
+ *                         + (c%2)*2 + (k%32)/16;
+ *            g[r] as in LOGICAL.
+ *          One 64-lane load of 16 bytes per lane then fetches one contiguous
+ *          1 KiB: 32 rows x 64 columns, lane (h*32 + rl) holding row rl,
+ *          columns [64c + 32h, 64c + 32h + 32). */
+enum { NVFP4_LAYOUT_LOGICAL = 0, NVFP4_LAYOUT_GEMM = 1 };
+
+/* Layer configuration (host struct). */
+typedef struct {
+    int32_t hidden;      /* H: multiple of 128 */
+    int32_t inter;       /* I: expert intermediate size, multiple of 128 */
+    int32_t n_experts;   /* E: 1..1024 */
+    int32_t top_k;       /* K: 1..n_experts (and <= 32) */
+    int32_t max_tokens;  /* bound on T; sizes the workspace (static capacity) */
+    int32_t scale_round; /* NVFP4_SCALE_RU or NVFP4_SCALE_RNE */
+} nvfp4moe_config;
+
+/* A quantized tensor of n_mats matrices [rows, cols] (host struct, device
+ * pointers).  Plane sizes: codes n_mats*rows*cols/2 bytes, scales
+ * n_mats*rows*cols/16 bytes, g n_mats*rows floats.  Matrices are stacked
+ * along rows, so matrix e's row n is row e*rows + n of the planes. */
+typedef struct {
+    uint8_t* codes;
+    uint8_t* scales;
+    float* g;
+    int32_t n_mats;
+    int32_t rows;
+    int32_t cols;
+    int32_t layout; /* NVFP4_LAYOUT_* */
+} nvfp4_qtensor;
+
+/* Human-readable name of a status code (static string). */
+NVFP4MOE_API const char* nvfp4_status_str(int status);
+
+/* Quantize each row of x [rows, cols] (row stride ld elements) into NVFP4
+ * (miniTE page, "how it differs": per-row outer scale g = max|row|/(6*448),
+ * 16-element E4M3 block scales, E2M1 codes, round to nearest even, no
+ * stochastic rounding).  Numeric contract, in binary32 with IEEE division:
+ *   g = amax/2688; d = 6*g; per block v = amax_b/d, s = E4M3(v) per
+ *   scale_round (0 if amax_b == 0); per element q = |x|/(s*g) and the code is
+ *   the nearest E2M1 value, ties to even, saturating at 6, carrying the input
+ *   sign bit; if s*g == 0 the code keeps only the sign.  A zero row gets
+ *   g = 0 and all scales 0.
+ * Requirements: cols % 16 == 0 (LOGICAL) or rows % 32 == 0 and
+ * cols % 128 == 0 (GEMM); ld >= cols; x 16-byte aligned and ld % 8 == 0.
+ * Output planes as described for the layout. */
+NVFP4MOE_API int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
+                   float* g, int32_t layout, int32_t scale_round, void* stream);
+
+/* Bytes of one quantized expert-weight tensor: which = 1 for W1 [E, 2I, H]
+ * (rows 0..I-1 of each expert are the gate projection, I..2I-1 the up
+ * projection), which = 2 for W2 [E, H, I].  Sum of the three planes, each
+ * rounded up to 256 bytes.  Returns 0 for an invalid config. */
+NVFP4MOE_API size_t nvfp4moe_weight_bytes(const nvfp4moe_config* cfg, int32_t which);
+
+/* Quantize BF16 expert weights (w1 [E, 2I, H], w2 [E, H, I]) in place into
+ * caller-owned GEMM-layout tensors (W1q: n_mats E, rows 2I, cols H; W2q:
+ * n_mats E, rows H, cols I).  Used once per weight update; writing into the
+ * same buffers keeps their addresses (article, section 4.6). */
+NVFP4MOE_API int nvfp4moe_quantize_weights(const nvfp4moe_config* cfg, const uint16_t* w1, const uint16_t* w2,
+                              const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q, void* stream);
+
+/* Workspace bytes for the forward; depends on cfg only (max_tokens bounds T),
+ * so one allocation serves every batch size.  Returns 0 for an invalid cfg. */
+NVFP4MOE_API size_t nvfp4moe_workspace_bytes(const nvfp4moe_config* cfg);
+
+/* The NVFP4 MoE expert forward for T tokens.
+ *   x      [T, H] BF16 activations (16-byte aligned)
+ *   ids    [T, K] int32 expert ids, each in [0, E), distinct within a token
+ *   probs  [T, K] float32 router probabilities (applied to the SwiGLU output)
+ *   W1q, W2q quantized weights in GEMM layout (nvfp4moe_quantize_weights)
+ *   out    [T, H] BF16; out[t] = bf16(FP32 sum over k = 0..K-1, in the order
+ *          the columns of ids list them, of expert ids[t,k]'s FC2 output)
+ * T == 0 is a no-op.  An expert with no tokens reads none of its weights.
+ * No host synchronisation; the launch grids depend on cfg and T only.
+ * Out-of-range or repeated ids do not fault: they set the device error word
+ * (nvfp4moe_device_error); the outputs are then unspecified. */
+NVFP4MOE_API int nvfp4moe_moe_expert_forward(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids,
+                                const float* probs, const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q,
+                                uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device error word of the last forward that used `workspace`: 0 if clean,
+ * else a bitwise OR of 1 (an id outside [0, E)) and 2 (an id repeated within a
+ * token).  Syncs `stream`.  *code_host (host) receives the word. */
+NVFP4MOE_API int nvfp4moe_device_error(const nvfp4moe_config* cfg, const void* workspace, int32_t* code_host, void* stream);
+
+/* Byte offsets of the forward's intermediates inside the workspace, for
+ * inspection (host struct).  Row-indexed buffers are indexed by sorted row r
+ * in [0, off[E]); pair p = t*K + k. */
+typedef struct {
+    size_t err;          /* int32 error word */
+    size_t expert_count; /* int32 [E] tokens routed to each expert */
+    size_t expert_off;   /* int32 [E+1] padded row offsets (device offsets of expert boundaries) */
+    size_t pair2row;     /* int32 [T*K] sorted row of each pair */
+    size_t row2pair;     /* int32 [rows_cap] pair of each sorted row, -1 for padding */
+    size_t a1_codes, a1_scales, a1_g;  /* quantized sorted X, GEMM layout, rows_cap rows x H */
+    size_t h;            /* BF16 [rows_cap, I] router-weighted SwiGLU output */
+    size_t amax2_part;   /* float [rows_cap, n_part] per-column-tile maxima of |h| */
+    size_t a2_codes, a2_scales, a2_g;  /* quantized h, GEMM layout, rows_cap rows x I */
+    size_t y2;           /* BF16 [rows_cap, H] FC2 output per sorted row */
+    int64_t rows_cap;    /* max_tokens*K + E*(m_align-1), rounded up to m_align */
+    int32_t m_align;     /* each expert's rows are padded to a multiple of this */
+    int32_t n_part;      /* column tiles of FC1 per row (entries of amax2_part per row) */
+} nvfp4moe_ws_layout;
+
+NVFP4MOE_API int nvfp4moe_workspace_layout(const nvfp4moe_config* cfg, nvfp4moe_ws_layout* layout_host);
+
+/* Dense NVFP4 linear: out [M, N] = bf16((Q(x) . Wq^T) * g^x * g^w), with
+ * x [M, K] BF16 and Wq one GEMM-layout matrix [N, K] (n_mats 1).  The
+ * activation quantization uses scale_round.  M >= 0, K % 128 == 0,
+ * N % 128 == 0. */
+NVFP4MOE_API size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K);
+NVFP4MOE_API int nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const nvfp4_qtensor* Wq, uint16_t* out,
+                 int32_t scale_round, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bitwise batch-invariance self-test (article, section 4.4: a row's result
+ * must not depend on its neighbours).  Draws n_probe probe tokens and filler
+ * tokens from `seed` on the host (a counter-based generator), runs every probe
+ * alone, in decode batches of every size 1..max_decode_batch with the probe
+ * at a varying position among fillers, and inside one prefill batch of
+ * prefill_tokens tokens holding all probes; then compares each probe's output
+ * bits with its batch-1 result.  Allocates its own device buffers (it is not
+ * a forward-path call) and syncs.  report_host (host, may be NULL) receives
+ * {n_compared, n_mismatched_tokens, first_bad_probe, first_bad_batch}.
+ * Returns NVFP4_OK when every bit matches, NVFP4_E_MISMATCH otherwise. */
+NVFP4MOE_API int nvfp4moe_selftest_batch_invariance(const nvfp4moe_config* cfg, const nvfp4_qtensor* W1q,
+                                       const nvfp4_qtensor* W2q, uint64_t seed, int32_t n_probe,
+                                       int32_t max_decode_batch, int32_t prefill_tokens, int64_t* report_host,
+                                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4MOE_H */

@@ -1,0 +1,321 @@
+// api.hip -- host side of the C ABI declared in include/nvfp4moe.h: argument
+// checks (before any launch), workspace carving, launch order, self-test.
+//
+// The forward enqueues, on the caller's stream and with no host sync:
+//   route_hist -> route_scan -> route_scatter (sort + amax + quantize X into
+//   the padded GEMM-layout buffer) -> FC1 grouped GEMM with the router-weighted
+//   SwiGLU producer (h and its per-tile maxima) -> quantize h -> FC2 grouped
+//   GEMM -> slot-order combine.
+// (miniTE summary page, "how to use it"; article sections 4.4-4.6.)
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "../../include/nvfp4moe.h"
+#include "nvfp4_kernels.h"
+
+using namespace nvfp4;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool cfg_ok(const nvfp4moe_config* c) {
+    if (!c) return false;
+    if (c->hidden <= 0 || c->hidden % 128 != 0) return false;
+    if (c->inter <= 0 || c->inter % 128 != 0) return false;
+    if (c->n_experts < 1 || c->n_experts > kMaxExperts) return false;
+    if (c->top_k < 1 || c->top_k > kMaxTopK || c->top_k > c->n_experts) return false;
+    if (c->max_tokens < 0) return false;
+    if (c->scale_round != NVFP4_SCALE_RU && c->scale_round != NVFP4_SCALE_RNE) return false;
+    const int64_t rows = (int64_t)c->max_tokens * c->top_k + (int64_t)c->n_experts * (kMAlign - 1);
+    if (rows >= (int64_t)1 << 30) return false;  // sorted row indices are int32
+    return true;
+}
+
+struct Layout {
+    nvfp4moe_ws_layout pub;
+    size_t blk_err, blk_counts, mtiles, n_mtiles, row_prob;
+    int64_t nblk_cap, mtiles_cap;
+    size_t total;
+};
+
+Layout make_layout(const nvfp4moe_config* c) {
+    Layout L{};
+    const int64_t E = c->n_experts, K = c->top_k, H = c->hidden, I = c->inter, Tm = c->max_tokens;
+    const int64_t P = Tm * K;
+    const int64_t rows = up((size_t)(P + E * (kMAlign - 1)), kMAlign);
+    L.nblk_cap = std::max<int64_t>(1, (Tm + kTokPerBlk - 1) / kTokPerBlk);
+    L.mtiles_cap = rows / kTileRows + E + 1;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = up(o + std::max<size_t>(bytes, 1), kAlign);
+        return at;
+    };
+    L.pub.err = take(4);
+    L.blk_err = take(4 * L.nblk_cap);
+    L.blk_counts = take(4 * L.nblk_cap * E);
+    L.pub.expert_count = take(4 * E);
+    L.pub.expert_off = take(4 * (E + 1));
+    L.n_mtiles = take(4);
+    L.mtiles = take(16 * L.mtiles_cap);
+    L.pub.pair2row = take(4 * std::max<int64_t>(P, 1));
+    L.pub.row2pair = take(4 * rows);
+    L.row_prob = take(4 * rows);
+    L.pub.a1_codes = take(rows * H / 2);
+    L.pub.a1_scales = take(rows * H / 16);
+    L.pub.a1_g = take(4 * rows);
+    L.pub.h = take(2 * rows * I);
+    L.pub.amax2_part = take(4 * rows * (I / 64));
+    L.pub.a2_codes = take(rows * I / 2);
+    L.pub.a2_scales = take(rows * I / 16);
+    L.pub.a2_g = take(4 * rows);
+    L.pub.y2 = take(2 * rows * H);
+    L.pub.rows_cap = rows;
+    L.pub.m_align = kMAlign;
+    L.pub.n_part = (int32_t)(I / 64);
+    L.total = o;
+    return L;
+}
+
+bool qt_ok(const nvfp4_qtensor* q, int64_t n_mats, int64_t rows, int64_t cols) {
+    return q && q->codes && q->scales && q->g && q->n_mats == n_mats && q->rows == rows && q->cols == cols &&
+           q->layout == NVFP4_LAYOUT_GEMM;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_E_HIP; }
+
+int grid_waves(int64_t tiles_bound) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    const int64_t cap = (int64_t)cus * 4;  // one 512-register wave per SIMD
+    return (int)std::max<int64_t>(8, std::min<int64_t>(tiles_bound, cap));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_str(int s) {
+    switch (s) {
+        case NVFP4_OK: return "ok";
+        case NVFP4_E_NULL: return "null pointer";
+        case NVFP4_E_SHAPE: return "invalid shape";
+        case NVFP4_E_ALIGN: return "misaligned pointer";
+        case NVFP4_E_WORKSPACE: return "workspace too small";
+        case NVFP4_E_CAPACITY: return "token count exceeds max_tokens";
+        case NVFP4_E_HIP: return "HIP error";
+        case NVFP4_E_MISMATCH: return "batch-invariance mismatch";
+        case NVFP4_E_DEVICE: return "device-side contract violation";
+        case NVFP4_E_ARG: return "invalid enum argument";
+        default: return "unknown status";
+    }
+}
+
+int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
+                   float* g, int32_t layout, int32_t scale_round, void* stream) {
+    if (layout != NVFP4_LAYOUT_LOGICAL && layout != NVFP4_LAYOUT_GEMM) return NVFP4_E_ARG;
+    if (scale_round != NVFP4_SCALE_RU && scale_round != NVFP4_SCALE_RNE) return NVFP4_E_ARG;
+    if (rows < 0 || cols <= 0 || cols % 16 != 0 || ld < cols) return NVFP4_E_SHAPE;
+    if (layout == NVFP4_LAYOUT_GEMM && (rows % 32 != 0 || cols % 128 != 0)) return NVFP4_E_SHAPE;
+    if (rows >= ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
+    if (rows == 0) return NVFP4_OK;
+    if (!x || !codes || !scales || !g) return NVFP4_E_NULL;
+    if (!aligned(x, 16) || ld % 8 != 0 || !aligned(codes, 4) || !aligned(g, 4)) return NVFP4_E_ALIGN;
+    return hip_status(launch_quant_rows(x, rows, cols, ld, codes, scales, g, layout == NVFP4_LAYOUT_GEMM,
+                                        scale_round == NVFP4_SCALE_RU, (hipStream_t)stream));
+}
+
+size_t nvfp4moe_weight_bytes(const nvfp4moe_config* cfg, int32_t which) {
+    if (!cfg_ok(cfg) || (which != 1 && which != 2)) return 0;
+    const size_t E = cfg->n_experts, H = cfg->hidden, I = cfg->inter;
+    const size_t rows = which == 1 ? E * 2 * I : E * H;
+    const size_t cols = which == 1 ? H : I;
+    return up(rows * cols / 2, kAlign) + up(rows * cols / 16, kAlign) + up(rows * 4, kAlign);
+}
+
+int nvfp4moe_quantize_weights(const nvfp4moe_config* cfg, const uint16_t* w1, const uint16_t* w2,
+                              const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q, void* stream) {
+    if (!cfg) return NVFP4_E_NULL;
+    if (!cfg_ok(cfg)) return NVFP4_E_SHAPE;
+    const int64_t E = cfg->n_experts, H = cfg->hidden, I = cfg->inter;
+    if (!w1 || !w2 || !W1q || !W2q) return NVFP4_E_NULL;
+    if (!qt_ok(W1q, E, 2 * I, H) || !qt_ok(W2q, E, H, I)) return NVFP4_E_SHAPE;
+    const bool ru = cfg->scale_round == NVFP4_SCALE_RU;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_quant_rows(w1, E * 2 * I, H, H, W1q->codes, W1q->scales, W1q->g, true, ru, s);
+    if (e != hipSuccess) return NVFP4_E_HIP;
+    return hip_status(launch_quant_rows(w2, E * H, I, I, W2q->codes, W2q->scales, W2q->g, true, ru, s));
+}
+
+size_t nvfp4moe_workspace_bytes(const nvfp4moe_config* cfg) {
+    if (!cfg_ok(cfg)) return 0;
+    return make_layout(cfg).total;
+}
+
+int nvfp4moe_workspace_layout(const nvfp4moe_config* cfg, nvfp4moe_ws_layout* out) {
+    if (!cfg || !out) return NVFP4_E_NULL;
+    if (!cfg_ok(cfg)) return NVFP4_E_SHAPE;
+    *out = make_layout(cfg).pub;
+    return NVFP4_OK;
+}
+
+int nvfp4moe_moe_expert_forward(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids,
+                                const float* probs, const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q,
+                                uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!cfg) return NVFP4_E_NULL;
+    if (!cfg_ok(cfg)) return NVFP4_E_SHAPE;
+    if (T < 0) return NVFP4_E_SHAPE;
+    if (T > cfg->max_tokens) return NVFP4_E_CAPACITY;
+    const int64_t E = cfg->n_experts, K = cfg->top_k, H = cfg->hidden, I = cfg->inter;
+    if (!W1q || !W2q) return NVFP4_E_NULL;
+    if (!qt_ok(W1q, E, 2 * I, H) || !qt_ok(W2q, E, H, I)) return NVFP4_E_SHAPE;
+    if (!workspace) return NVFP4_E_NULL;
+    const Layout L = make_layout(cfg);
+    if (workspace_bytes < L.total) return NVFP4_E_WORKSPACE;
+    if (!aligned(workspace, kAlign)) return NVFP4_E_ALIGN;
+    if (T == 0) return NVFP4_OK;
+    if (!x || !ids || !probs || !out) return NVFP4_E_NULL;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ids, 4) || !aligned(probs, 4)) return NVFP4_E_ALIGN;
+
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+    RouteBuffers rb;
+    rb.blk_counts = (int32_t*)(ws + L.blk_counts);
+    rb.blk_err = (int32_t*)(ws + L.blk_err);
+    rb.expert_count = (int32_t*)(ws + L.pub.expert_count);
+    rb.expert_off = (int32_t*)(ws + L.pub.expert_off);
+    rb.mtiles = (int4*)(ws + L.mtiles);
+    rb.n_mtiles = (int32_t*)(ws + L.n_mtiles);
+    rb.err_word = (int32_t*)(ws + L.pub.err);
+    rb.pair2row = (int32_t*)(ws + L.pub.pair2row);
+    rb.row2pair = (int32_t*)(ws + L.pub.row2pair);
+    rb.row_prob = (float*)(ws + L.row_prob);
+    rb.a_codes = ws + L.pub.a1_codes;
+    rb.a_scales = ws + L.pub.a1_scales;
+    rb.a_g = (float*)(ws + L.pub.a1_g);
+    const bool ru = cfg->scale_round == NVFP4_SCALE_RU;
+
+    hipError_t e = launch_route(x, ids, probs, T, (int32_t)H, (int32_t)K, (int32_t)E, ru, rb, s);
+    if (e != hipSuccess) return NVFP4_E_HIP;
+
+    // Static bound on row tiles for this T (the device count is <= this).
+    const int64_t mt_bound = ((int64_t)T * K + E * (kMAlign - 1)) / kTileRows + E + 1;
+
+    GemmParams f1{};
+    f1.a_codes = rb.a_codes;
+    f1.a_scales = rb.a_scales;
+    f1.a_g = rb.a_g;
+    f1.b_codes = W1q->codes;
+    f1.b_scales = W1q->scales;
+    f1.b_g = W1q->g;
+    f1.K = (int32_t)H;
+    f1.N = (int32_t)(2 * I);
+    f1.n_tiles_n = (int32_t)(I / 64);
+    f1.mtiles = rb.mtiles;
+    f1.n_mtiles = rb.n_mtiles;
+    f1.dense_m = -1;
+    f1.out = (uint16_t*)(ws + L.pub.h);
+    f1.ld_out = I;
+    f1.row_prob = rb.row_prob;
+    f1.amax_part = (float*)(ws + L.pub.amax2_part);
+    f1.inter = (int32_t)I;
+    e = launch_gemm(kGemmSwiGLU, f1, grid_waves(mt_bound * f1.n_tiles_n), s);
+    if (e != hipSuccess) return NVFP4_E_HIP;
+
+    uint8_t* a2c = ws + L.pub.a2_codes;
+    uint8_t* a2s = ws + L.pub.a2_scales;
+    float* a2g = (float*)(ws + L.pub.a2_g);
+    e = launch_quant_h(f1.out, (int64_t)T * K, I, rb.pair2row, f1.amax_part, f1.n_tiles_n, a2c, a2s, a2g, ru, s);
+    if (e != hipSuccess) return NVFP4_E_HIP;
+
+    GemmParams f2{};
+    f2.a_codes = a2c;
+    f2.a_scales = a2s;
+    f2.a_g = a2g;
+    f2.b_codes = W2q->codes;
+    f2.b_scales = W2q->scales;
+    f2.b_g = W2q->g;
+    f2.K = (int32_t)I;
+    f2.N = (int32_t)H;
+    f2.n_tiles_n = (int32_t)(H / 128);
+    f2.mtiles = rb.mtiles;
+    f2.n_mtiles = rb.n_mtiles;
+    f2.dense_m = -1;
+    f2.out = (uint16_t*)(ws + L.pub.y2);
+    f2.ld_out = H;
+    e = launch_gemm(kGemmPlain, f2, grid_waves(mt_bound * f2.n_tiles_n), s);
+    if (e != hipSuccess) return NVFP4_E_HIP;
+
+    return hip_status(launch_combine(f2.out, rb.pair2row, T, (int32_t)H, (int32_t)K, out, s));
+}
+
+int nvfp4moe_device_error(const nvfp4moe_config* cfg, const void* workspace, int32_t* code_host, void* stream) {
+    if (!cfg || !workspace || !code_host) return NVFP4_E_NULL;
+    if (!cfg_ok(cfg)) return NVFP4_E_SHAPE;
+    const Layout L = make_layout(cfg);
+    hipStream_t s = (hipStream_t)stream;
+    int32_t v = 0;
+    if (hipMemcpyAsync(&v, (const uint8_t*)workspace + L.pub.err, 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+        return NVFP4_E_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return NVFP4_E_HIP;
+    *code_host = v;
+    return NVFP4_OK;
+}
+
+size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K) {
+    if (M < 0 || K <= 0 || K % 128 != 0) return 0;
+    const size_t rows = up((size_t)std::max<int64_t>(M, 1), 32);
+    return up(rows * K / 2, kAlign) + up(rows * K / 16, kAlign) + up(rows * 4, kAlign);
+}
+
+int nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const nvfp4_qtensor* Wq, uint16_t* out,
+                 int32_t scale_round, void* workspace, size_t workspace_bytes, void* stream) {
+    if (scale_round != NVFP4_SCALE_RU && scale_round != NVFP4_SCALE_RNE) return NVFP4_E_ARG;
+    if (M < 0 || K <= 0 || K % 128 != 0 || M >= ((int64_t)1 << 30)) return NVFP4_E_SHAPE;
+    if (!Wq) return NVFP4_E_NULL;
+    if (!Wq->codes || !Wq->scales || !Wq->g) return NVFP4_E_NULL;
+    if (Wq->n_mats != 1 || Wq->cols != K || Wq->rows <= 0 || Wq->rows % 128 != 0 || Wq->layout != NVFP4_LAYOUT_GEMM)
+        return NVFP4_E_SHAPE;
+    if (!workspace) return NVFP4_E_NULL;
+    if (workspace_bytes < nvfp4_linear_workspace_bytes(M, K)) return NVFP4_E_WORKSPACE;
+    if (!aligned(workspace, kAlign)) return NVFP4_E_ALIGN;
+    if (M == 0) return NVFP4_OK;
+    if (!x || !out) return NVFP4_E_NULL;
+    if (!aligned(x, 16) || !aligned(out, 4)) return NVFP4_E_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    const size_t rows = up((size_t)M, 32);
+    uint8_t* ws = (uint8_t*)workspace;
+    uint8_t* xc = ws;
+    uint8_t* xs = ws + up(rows * K / 2, kAlign);
+    float* xg = (float*)(ws + up(rows * K / 2, kAlign) + up(rows * K / 16, kAlign));
+    hipError_t e = launch_quant_rows(x, M, K, K, xc, xs, xg, true, scale_round == NVFP4_SCALE_RU, s);
+    if (e != hipSuccess) return NVFP4_E_HIP;
+    GemmParams p{};
+    p.a_codes = xc;
+    p.a_scales = xs;
+    p.a_g = xg;
+    p.b_codes = Wq->codes;
+    p.b_scales = Wq->scales;
+    p.b_g = Wq->g;
+    p.K = (int32_t)K;
+    p.N = Wq->rows;
+    p.n_tiles_n = Wq->rows / 128;
+    p.dense_m = (int32_t)M;
+    p.out = out;
+    p.ld_out = Wq->rows;
+    const int64_t tiles = (M + kTileRows - 1) / kTileRows * p.n_tiles_n;
+    return hip_status(launch_gemm(kGemmPlain, p, grid_waves(tiles), s));
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// nvfp4_device.h -- device helpers shared by the gfx950 kernels: NVFP4 format
+// encoders, the GEMM-layout address map and wave reductions.
+//
+// Formats (miniTE summary page, section "how it differs"): E2M1 element codes,
+// one OCP E4M3FN scale per 16 elements, one FP32 outer scale per row
+// g = max|row| / (6*448), round to nearest, no stochastic rounding.  The E4M3
+// rounding of the block scale is a build-time reading (round up by default,
+// RNE selectable); both are exact integer/bit manipulations below.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4_kernels.h"
+
+namespace nvfp4 {
+
+constexpr int kWave = 64;
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> BF16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// E4M3FN byte of a non-negative block scale v.  round_up: the smallest E4M3FN
+// value >= v; otherwise nearest with ties to an even mantissa.  Clamped to
+// 448 (0x7E); 0 for v <= 0.
+__device__ __forceinline__ uint32_t e4m3_encode(float v, bool round_up) {
+    if (!(v > 0.0f)) return 0u;
+    if (v >= 448.0f) return 0x7Eu;
+    if (v < 0.015625f) {                       // below 2^-6: subnormal codes m * 2^-9, m = 0..8
+        float t = v * 512.0f;                  // exact power-of-two scaling
+        float m = round_up ? ceilf(t) : rintf(t);
+        return (uint32_t)m;                    // m == 8 is 2^-6, whose byte is 0x08
+    }
+    uint32_t u = __float_as_uint(v);
+    int e = (int)(u >> 23) - 127;              // -6 .. 8
+    float t = __uint_as_float((u & 0x007FFFFFu) | (130u << 23));  // 8 * 1.mantissa, in [8, 16)
+    float m = round_up ? ceilf(t) : rintf(t);  // 8 .. 16
+    uint32_t mi = (uint32_t)m;
+    if (mi == 16u) {
+        mi = 8u;
+        e += 1;
+    }
+    if (e > 8 || (e == 8 && mi > 14u)) return 0x7Eu;
+    return ((uint32_t)(e + 7) << 3) | (mi - 8u);
+}
+
+// E4M3FN byte -> float (gfx950 converts the OCP E4M3FN format in hardware).
+__device__ __forceinline__ float e4m3_decode(uint32_t byte) { return __builtin_amdgcn_cvt_f32_fp8(byte, 0); }
+
+// E2M1 magnitude code of q >= 0: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6},
+// ties to the even code, saturating.  Each comparison is one decision
+// threshold; '>' at a tie keeps the lower (even) code, '>=' takes the upper.
+__device__ __forceinline__ uint32_t e2m1_magnitude(float q) {
+    return (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f) + (uint32_t)(q > 1.25f) + (uint32_t)(q >= 1.75f) +
+           (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) + (uint32_t)(q > 5.0f);
+}
+
+// --- GEMM layout (see include/nvfp4moe.h) -------------------------------------------------------
+// Byte offset of the 4-byte group holding columns [k, k+8) (k % 8 == 0) of row r.
+__device__ __forceinline__ size_t gemm_code_off(int64_t r, int64_t k, int64_t cols) {
+    int64_t rt = r >> 5, rl = r & 31, c = k >> 6, h = (k >> 5) & 1;
+    return (size_t)((rt * (cols >> 6) + c) * 1024 + (h * 32 + rl) * 16 + ((k & 31) >> 1));
+}
+// Byte offset of the scale of the 16-column block starting at column k of row r.
+__device__ __forceinline__ size_t gemm_scale_off(int64_t r, int64_t k, int64_t cols) {
+    int64_t rt = r >> 5, rl = r & 31, c = k >> 6, h = (k >> 5) & 1;
+    return (size_t)((rt * (cols >> 7) + (c >> 1)) * 256 + (h * 32 + rl) * 4 + (c & 1) * 2 + ((k & 31) >> 4));
+}
+
+// --- wave reductions ----------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+}  // namespace nvfp4

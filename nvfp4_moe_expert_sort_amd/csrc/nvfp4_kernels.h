@@ -1,0 +1,63 @@
+// nvfp4_kernels.h -- internal launchers of the gfx950 kernels (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kMAlign = 32;      // each expert's rows are padded to a multiple of this (one MFMA row tile)
+constexpr int kTileRows = 128;   // rows per GEMM wave tile (4 MFMA row tiles)
+constexpr int kTokPerBlk = 16;   // tokens per block in the sort kernels
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kGemmPlain = 0;   // y = bf16(acc * g_a * g_b)
+constexpr int kGemmSwiGLU = 1;  // FC1 + router-weighted SwiGLU producer (h and per-tile |h| maxima)
+
+struct GemmParams {
+    const uint8_t* a_codes;
+    const uint8_t* a_scales;
+    const float* a_g;
+    const uint8_t* b_codes;
+    const uint8_t* b_scales;
+    const float* b_g;
+    int32_t K;          // reduction length, multiple of 128
+    int32_t N;          // rows of one expert's weight matrix
+    int32_t n_tiles_n;  // column tiles per row tile
+    const int4* mtiles;        // row tiles {row0, expert, 32-row subtiles, end of valid rows}
+    const int32_t* n_mtiles;   // device count of row tiles
+    int32_t dense_m;           // >= 0: one matrix with this many rows; row tiles implied
+    uint16_t* out;
+    int64_t ld_out;
+    const float* row_prob;     // SwiGLU mode: router probability per row
+    float* amax_part;          // SwiGLU mode: [rows][n_tiles_n] max |h|
+    int32_t inter;             // SwiGLU mode: I (gate rows [0, I), up rows [I, 2I))
+};
+
+struct RouteBuffers {
+    int32_t* blk_counts;   // [nblk][E]; exclusive per-expert prefix after the scan
+    int32_t* blk_err;      // [nblk]
+    int32_t* expert_count; // [E]
+    int32_t* expert_off;   // [E+1]
+    int4* mtiles;          // [mtiles_cap]
+    int32_t* n_mtiles;     // [1]
+    int32_t* err_word;     // [1]
+    int32_t* pair2row;     // [T*K]
+    int32_t* row2pair;     // [rows_cap]
+    float* row_prob;       // [rows_cap]
+    uint8_t* a_codes;
+    uint8_t* a_scales;
+    float* a_g;
+};
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
+                             uint8_t* scales, float* g, bool gemm, bool round_up, hipStream_t stream);
+hipError_t launch_quant_h(const uint16_t* h, int64_t P, int64_t I, const int32_t* pair2row, const float* amax2_part,
+                          int n_part, uint8_t* codes, uint8_t* scales, float* g, bool round_up, hipStream_t stream);
+hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* probs, int32_t T, int32_t H, int32_t K,
+                        int32_t E, bool round_up, const RouteBuffers& rb, hipStream_t stream);
+hipError_t launch_gemm(int mode, const GemmParams& P, int grid_waves, hipStream_t stream);
+hipError_t launch_combine(const uint16_t* y2, const int32_t* pair2row, int32_t T, int32_t H, int32_t K,
+                          uint16_t* out, hipStream_t stream);
+
+}  // namespace nvfp4
