@@ -1,0 +1,218 @@
+"""Benchmark of the NVFP4 MoE expert forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one whole forward (sort + quantize X, FC1 with the SwiGLU producer,
+quantize h, FC2, combine) over the Qwen3-30B-A3B-shaped layer with 4096
+tokens (hidden 2048, 128 experts, top-8, expert intermediate 768; synthetic
+seeded inputs and random weights, resident in HBM before timing).  W untimed
+warm-up steps, then exactly K steps bracketed by device synchronisation.
+Prints one JSON line.  The dominant kernel (FC1) is timed live inside the
+timed region with HIP events recorded on the forward's stream at its
+boundaries; the CPU oracle is timed on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense f16/bf16 MFMA
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 MFMA (reported for context)
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--tokens", type=int, default=4096)
+    ap.add_argument("--cold-steps", type=int, default=10, help="extra forwards timed after a cache-evicting write")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference dispatch for HBM byte counters)")
+    return ap.parse_args()
+
+
+def layer_bytes(T, H, E, K, I, counts):
+    """Algorithmic HBM bytes of the layer as built (each intermediate written and read once)."""
+    P = T * K
+    qrow = lambda c: c // 2 + c // 16 + 4  # noqa: E731  packed codes + scales + g
+    used = int((counts > 0).sum())
+    w = used * (2 * I * qrow(H) + H * qrow(I))
+    x_in, out = T * H * 2, T * H * 2
+    a1, h, a2, y2 = P * qrow(H), P * I * 2, P * qrow(I), P * H * 2
+    routing = T * K * 8
+    return dict(weights=w, total=w + x_in + out + routing + 2 * (a1 + h + a2 + y2),
+                fc1=a1 + used * 2 * I * qrow(H) + h, compulsory=w + x_in + out + routing)
+
+
+PROFILE = os.path.join(ROOT, "profiles", "moe_forward_qwen3_T4096.md")
+FC1_SOURCES = ["nvfp4_moe_expert_sort_amd/csrc/gemm.hip", "nvfp4_moe_expert_sort_amd/csrc/nvfp4_device.h",
+               "nvfp4_moe_expert_sort_amd/csrc/nvfp4_kernels.h"]
+
+
+def fc1_traffic_bytes():
+    """HBM bytes per FC1 launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    or None when the kernel sources changed since those counters were taken."""
+    import hashlib
+    try:
+        text = open(PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(line.strip().split(": ", 1) for line in text.splitlines()
+                  if line.strip().startswith(("fc1_traffic_bytes_per_launch:", "kernel_source_sha256:")))
+    h = hashlib.sha256()
+    for f in FC1_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("kernel_source_sha256") != h.hexdigest() or "fc1_traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["fc1_traffic_bytes_per_launch"])
+
+
+def cpu_baseline(wl, w1, w2, target_s):
+    import oracle
+    T = wl.shape.T
+    wts = oracle.DequantWeights(w1, w2)  # weight quantization is outside the forward, as on the GPU
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.moe_forward(wl.x[:n], wl.ids[:n], wl.probs[:n], wts)
+        return time.perf_counter() - t0
+
+    n0 = 16
+    t_small = run(n0)
+    n = int(min(T, max(n0, n0 * target_s / max(t_small, 1e-3))))
+    t = run(n) if n != n0 else t_small
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    return {"value": n / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of {T} tokens of the same workload (all their top-{wl.shape.K} pairs), "
+                      f"weights pre-quantized and dequantized outside the timed region; {t:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the expert-parallel sharding across GPUs is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import moe_workloads as W
+    import nvfp4_moe_expert_sort_amd as m
+
+    dev = torch.device("cuda:0")
+    wl = W.qwen3(seed=2, T=args.tokens)
+    s = wl.shape
+    T, H, E, K, I = s.T, s.H, s.E, s.K, s.I
+    w1, w2 = wl.weights(threads=16)
+    cfg = m.make_config(H, I, E, K, T)
+    qw = m.QuantWeights(cfg, dev).quantize_from(torch.from_numpy(w1.view(np.int16)).to(dev),
+                                                torch.from_numpy(w2.view(np.int16)).to(dev))
+    ws = m.alloc_workspace(cfg, dev)
+    x = torch.from_numpy(wl.x.view(np.int16)).to(dev)
+    ids = torch.from_numpy(wl.ids).to(dev)
+    probs = torch.from_numpy(wl.probs).to(dev)
+    out = torch.empty((T, H), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    if args.calibrate_copy:
+        src = torch.ones((1 << 30,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        m.moe_expert_forward(cfg, x, ids, probs, qw, ws, out=out)
+    torch.cuda.synchronize()
+    if m.device_error(cfg, ws) != 0:
+        raise RuntimeError("device error word set")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(m.N_STAGE_EVENTS)] for _ in range(args.steps)]
+    for ev in events:  # torch creates the underlying hipEvent on first record
+        for e in ev:
+            e.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        m.moe_expert_forward_events(cfg, x, ids, probs, qw, ws, events[k], out, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(m.N_STAGE_EVENTS - 1)] for ev in events])
+    stage_mean = stage_ms.mean(axis=0)
+
+    # Cold-cache forwards (secondary): a 512 MiB write evicts L2 and the 256 MB MALL before each one.
+    cold = []
+    if args.cold_steps > 0:
+        scratch = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(args.cold_steps):
+            scratch.fill_(1)
+            e0.record(stream)
+            m.moe_expert_forward(cfg, x, ids, probs, qw, ws, out=out)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del scratch
+
+    P = T * K
+    layer_flop = 2.0 * P * 3 * H * I
+    fc1_flop = 2.0 * P * H * 2 * I
+    fc2_flop = 2.0 * P * I * H
+    fc1_s = stage_mean[1] / 1e3
+    achieved = fc1_flop / fc1_s / 1e12
+    counts = wl.expert_counts()
+    byts = layer_bytes(T, H, E, K, I, counts)
+    layer_s = ms_per_step / 1e3
+    result = {
+        "metric": "NVFP4 MoE expert-forward tokens/s (FC1+FC2) and % of MFMA peak",
+        "value": T / layer_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4(e2m1 x e4m3) -> f16 mfma, fp32 accumulate",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) random weights, softmax top-8 routing)",
+        "config": {"workload": wl.name, "tokens": T, "hidden": H, "experts": E, "top_k": K, "inter": I,
+                   "seed": 2, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": fc1_traffic_bytes(),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "algorithmic_bytes": byts["fc1"],
+                     "kernel": "gemm_kernel<SwiGLU> (FC1 grouped GEMM + router-weighted SwiGLU producer)",
+                     "work_per_launch": f"2*T*K*H*2I = {fc1_flop:.4e} flop (useful rows only)",
+                     "avg_launch_ms": stage_mean[1]},
+        "layer": {"tflops": layer_flop / layer_s / 1e12,
+                  "frac_f16_mfma_peak": layer_flop / layer_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                  "frac_fp4_mfma_peak": layer_flop / layer_s / 1e12 / MFMA_FP4_PEAK_TFLOPS,
+                  "hbm_gbs_algorithmic": byts["total"] / layer_s / 1e9,
+                  "frac_hbm_peak": byts["total"] / layer_s / 1e9 / HBM_PEAK_GBS,
+                  "stage_ms": dict(zip(m.STAGES, [round(float(v), 4) for v in stage_mean])),
+                  "fc2_tflops": fc2_flop / (stage_mean[3] / 1e3) / 1e12,
+                  "cold_ms_median": float(np.median(cold)) if cold else None,
+                  "cold_tokens_per_s": T / (np.median(cold) / 1e3) if cold else None},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, w1, w2, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

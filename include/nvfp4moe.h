@@ -161,6 +161,18 @@ NVFP4MOE_API int nvfp4moe_moe_expert_forward(const nvfp4moe_config* cfg, const u
                                 const float* probs, const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q,
                                 uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same forward, recording caller-created hipEvent_t events[i] on `stream`
+ * at each stage boundary, for timing the stages inside a timed region
+ * (events[0] before the sort, [1] after the sort and the quantization of X,
+ * [2] after the FC1 GEMM with its SwiGLU producer, [3] after the quantization
+ * of h, [4] after the FC2 GEMM, [5] after the combine).  events (host array)
+ * must hold NVFP4MOE_N_STAGE_EVENTS non-null events.  No synchronisation. */
+#define NVFP4MOE_N_STAGE_EVENTS 6
+NVFP4MOE_API int nvfp4moe_moe_expert_forward_events(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T,
+                                                    const int32_t* ids, const float* probs, const nvfp4_qtensor* W1q,
+                                                    const nvfp4_qtensor* W2q, uint16_t* out, void* workspace,
+                                                    size_t workspace_bytes, void* const* events, void* stream);
+
 /* Device error word of the last forward that used `workspace`: 0 if clean,
  * else a bitwise OR of 1 (an id outside [0, E)) and 2 (an id repeated within a
  * token).  Syncs `stream`.  *code_host (host) receives the word. */

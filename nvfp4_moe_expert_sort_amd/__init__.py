@@ -23,7 +23,8 @@ LAYOUT_GEMM = 1
 
 # Every function the C header declares (checked against the header by the tests).
 EXPORTS = ["nvfp4_status_str", "nvfp4_quantize", "nvfp4moe_weight_bytes", "nvfp4moe_quantize_weights",
-           "nvfp4moe_workspace_bytes", "nvfp4moe_moe_expert_forward", "nvfp4moe_device_error",
+           "nvfp4moe_workspace_bytes", "nvfp4moe_moe_expert_forward", "nvfp4moe_moe_expert_forward_events",
+           "nvfp4moe_device_error",
            "nvfp4moe_workspace_layout", "nvfp4_linear_workspace_bytes", "nvfp4_linear",
            "nvfp4moe_selftest_batch_invariance"]
 
@@ -72,6 +73,8 @@ def lib():
         "nvfp4moe_quantize_weights": (ctypes.c_int, [cfgp, vp, vp, qtp, qtp, vp]),
         "nvfp4moe_workspace_bytes": (sz, [cfgp]),
         "nvfp4moe_moe_expert_forward": (ctypes.c_int, [cfgp, vp, i32, vp, vp, qtp, qtp, vp, vp, sz, vp]),
+        "nvfp4moe_moe_expert_forward_events": (ctypes.c_int, [cfgp, vp, i32, vp, vp, qtp, qtp, vp, vp, sz,
+                                                               ctypes.POINTER(vp), vp]),
         "nvfp4moe_device_error": (ctypes.c_int, [cfgp, vp, ctypes.POINTER(i32), vp]),
         "nvfp4moe_workspace_layout": (ctypes.c_int, [cfgp, ctypes.POINTER(WsLayout)]),
         "nvfp4_linear_workspace_bytes": (sz, [i64, i64]),
@@ -183,6 +186,22 @@ def moe_expert_forward(cfg: Config, x, ids, probs, weights: QuantWeights, worksp
                                            ctypes.byref(weights.W1q), ctypes.byref(weights.W2q), _ptr(out),
                                            _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "nvfp4moe_moe_expert_forward")
+    return out
+
+
+N_STAGE_EVENTS = 6
+STAGES = ["sort+quantize X", "FC1 + SwiGLU producer", "quantize h", "FC2", "combine"]
+
+
+def moe_expert_forward_events(cfg: Config, x, ids, probs, weights: QuantWeights, workspace, events, out,
+                              stream=None):
+    """nvfp4moe_moe_expert_forward_events: as moe_expert_forward, recording the
+    6 torch.cuda.Event objects in `events` at the stage boundaries on the stream."""
+    arr = (ctypes.c_void_p * N_STAGE_EVENTS)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    st = lib().nvfp4moe_moe_expert_forward_events(ctypes.byref(cfg), _ptr(x), x.shape[0], _ptr(ids), _ptr(probs),
+                                                  ctypes.byref(weights.W1q), ctypes.byref(weights.W2q), _ptr(out),
+                                                  _ptr(workspace), workspace.numel(), arr, _stream(stream))
+    _check(st, "nvfp4moe_moe_expert_forward_events")
     return out
 
 

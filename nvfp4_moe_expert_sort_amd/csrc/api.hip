@@ -170,9 +170,16 @@ int nvfp4moe_workspace_layout(const nvfp4moe_config* cfg, nvfp4moe_ws_layout* ou
     return NVFP4_OK;
 }
 
-int nvfp4moe_moe_expert_forward(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids,
-                                const float* probs, const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q,
-                                uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward; when `events` is non-null, events[i] is recorded on the stream
+// at each stage boundary (before the sort, after the sort, after FC1, after
+// the FC2-input quantizer, after FC2, after the combine).
+int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids, const float* probs,
+                 const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q, uint16_t* out, void* workspace,
+                 size_t workspace_bytes, void* stream, void* const* events) {
     if (!cfg) return NVFP4_E_NULL;
     if (!cfg_ok(cfg)) return NVFP4_E_SHAPE;
     if (T < 0) return NVFP4_E_SHAPE;
@@ -189,6 +196,9 @@ int nvfp4moe_moe_expert_forward(const nvfp4moe_config* cfg, const uint16_t* x, i
     if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ids, 4) || !aligned(probs, 4)) return NVFP4_E_ALIGN;
 
     hipStream_t s = (hipStream_t)stream;
+    auto mark = [&](int i) -> bool {
+        return !events || hipEventRecord((hipEvent_t)events[i], s) == hipSuccess;
+    };
     uint8_t* ws = (uint8_t*)workspace;
     RouteBuffers rb;
     rb.blk_counts = (int32_t*)(ws + L.blk_counts);
@@ -206,8 +216,9 @@ int nvfp4moe_moe_expert_forward(const nvfp4moe_config* cfg, const uint16_t* x, i
     rb.a_g = (float*)(ws + L.pub.a1_g);
     const bool ru = cfg->scale_round == NVFP4_SCALE_RU;
 
+    if (!mark(0)) return NVFP4_E_HIP;
     hipError_t e = launch_route(x, ids, probs, T, (int32_t)H, (int32_t)K, (int32_t)E, ru, rb, s);
-    if (e != hipSuccess) return NVFP4_E_HIP;
+    if (e != hipSuccess || !mark(1)) return NVFP4_E_HIP;
 
     // Static bound on row tiles for this T (the device count is <= this).
     const int64_t mt_bound = ((int64_t)T * K + E * (kMAlign - 1)) / kTileRows + E + 1;
@@ -231,13 +242,13 @@ int nvfp4moe_moe_expert_forward(const nvfp4moe_config* cfg, const uint16_t* x, i
     f1.amax_part = (float*)(ws + L.pub.amax2_part);
     f1.inter = (int32_t)I;
     e = launch_gemm(kGemmSwiGLU, f1, grid_waves(mt_bound * f1.n_tiles_n), s);
-    if (e != hipSuccess) return NVFP4_E_HIP;
+    if (e != hipSuccess || !mark(2)) return NVFP4_E_HIP;
 
     uint8_t* a2c = ws + L.pub.a2_codes;
     uint8_t* a2s = ws + L.pub.a2_scales;
     float* a2g = (float*)(ws + L.pub.a2_g);
     e = launch_quant_h(f1.out, (int64_t)T * K, I, rb.pair2row, f1.amax_part, f1.n_tiles_n, a2c, a2s, a2g, ru, s);
-    if (e != hipSuccess) return NVFP4_E_HIP;
+    if (e != hipSuccess || !mark(3)) return NVFP4_E_HIP;
 
     GemmParams f2{};
     f2.a_codes = a2c;
@@ -255,9 +266,31 @@ int nvfp4moe_moe_expert_forward(const nvfp4moe_config* cfg, const uint16_t* x, i
     f2.out = (uint16_t*)(ws + L.pub.y2);
     f2.ld_out = H;
     e = launch_gemm(kGemmPlain, f2, grid_waves(mt_bound * f2.n_tiles_n), s);
-    if (e != hipSuccess) return NVFP4_E_HIP;
+    if (e != hipSuccess || !mark(4)) return NVFP4_E_HIP;
 
-    return hip_status(launch_combine(f2.out, rb.pair2row, T, (int32_t)H, (int32_t)K, out, s));
+    e = launch_combine(f2.out, rb.pair2row, T, (int32_t)H, (int32_t)K, out, s);
+    if (e != hipSuccess || !mark(5)) return NVFP4_E_HIP;
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4moe_moe_expert_forward(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids,
+                                const float* probs, const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q,
+                                uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+    return forward_impl(cfg, x, T, ids, probs, W1q, W2q, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int nvfp4moe_moe_expert_forward_events(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids,
+                                       const float* probs, const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q,
+                                       uint16_t* out, void* workspace, size_t workspace_bytes, void* const* events,
+                                       void* stream) {
+    if (!events) return NVFP4_E_NULL;
+    for (int i = 0; i < NVFP4MOE_N_STAGE_EVENTS; i++)
+        if (!events[i]) return NVFP4_E_NULL;
+    return forward_impl(cfg, x, T, ids, probs, W1q, W2q, out, workspace, workspace_bytes, stream, events);
 }
 
 int nvfp4moe_device_error(const nvfp4moe_config* cfg, const void* workspace, int32_t* code_host, void* stream) {
