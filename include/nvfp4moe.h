@@ -124,7 +124,8 @@ NVFP4MOE_API const char* nvfp4_status_str(int status);
  *   sign bit; if s*g == 0 the code keeps only the sign.  A zero row gets
  *   g = 0 and all scales 0.
  * Requirements: cols % 16 == 0 (LOGICAL) or rows % 32 == 0 and
- * cols % 128 == 0 (GEMM); ld >= cols; x 16-byte aligned and ld % 8 == 0.
+ * cols % 128 == 0 (GEMM); ld >= cols; x 16-byte aligned and ld % 8 == 0;
+ * codes 16-byte, scales 2-byte and g 4-byte aligned.
  * Output planes as described for the layout. */
 NVFP4MOE_API int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
                    float* g, int32_t layout, int32_t scale_round, void* stream);
@@ -189,12 +190,12 @@ typedef struct {
     size_t row2pair;     /* int32 [rows_cap] pair of each sorted row, -1 for padding */
     size_t a1_codes, a1_scales, a1_g;  /* quantized sorted X, GEMM layout, rows_cap rows x H */
     size_t h;            /* BF16 [rows_cap, I] router-weighted SwiGLU output */
-    size_t amax2_part;   /* float [rows_cap, n_part] per-column-tile maxima of |h| */
+    size_t amax2_part;   /* float [rows_cap, n_part] max |h| of each 32-column group of h, per row */
     size_t a2_codes, a2_scales, a2_g;  /* quantized h, GEMM layout, rows_cap rows x I */
     size_t y2;           /* BF16 [rows_cap, H] FC2 output per sorted row */
     int64_t rows_cap;    /* max_tokens*K + E*(m_align-1), rounded up to m_align */
     int32_t m_align;     /* each expert's rows are padded to a multiple of this */
-    int32_t n_part;      /* column tiles of FC1 per row (entries of amax2_part per row) */
+    int32_t n_part;      /* I / 32: entries of amax2_part per row */
 } nvfp4moe_ws_layout;
 
 NVFP4MOE_API int nvfp4moe_workspace_layout(const nvfp4moe_config* cfg, nvfp4moe_ws_layout* layout_host);

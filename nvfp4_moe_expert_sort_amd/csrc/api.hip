@@ -39,7 +39,7 @@ bool cfg_ok(const nvfp4moe_config* c) {
 
 struct Layout {
     nvfp4moe_ws_layout pub;
-    size_t blk_err, blk_counts, mtiles, n_mtiles, row_prob;
+    size_t blk_err, blk_counts, mtiles, n_mtiles, row_prob, xq_codes, xq_scales, gx;
     int64_t nblk_cap, mtiles_cap;
     size_t total;
 };
@@ -67,18 +67,21 @@ Layout make_layout(const nvfp4moe_config* c) {
     L.pub.pair2row = take(4 * std::max<int64_t>(P, 1));
     L.pub.row2pair = take(4 * rows);
     L.row_prob = take(4 * rows);
+    L.xq_codes = take(std::max<int64_t>(Tm, 1) * H / 2);
+    L.xq_scales = take(std::max<int64_t>(Tm, 1) * H / 16);
+    L.gx = take(4 * std::max<int64_t>(Tm, 1));
     L.pub.a1_codes = take(rows * H / 2);
     L.pub.a1_scales = take(rows * H / 16);
     L.pub.a1_g = take(4 * rows);
     L.pub.h = take(2 * rows * I);
-    L.pub.amax2_part = take(4 * rows * (I / 64));
+    L.pub.amax2_part = take(4 * rows * (I / 32));
     L.pub.a2_codes = take(rows * I / 2);
     L.pub.a2_scales = take(rows * I / 16);
     L.pub.a2_g = take(4 * rows);
     L.pub.y2 = take(2 * rows * H);
     L.pub.rows_cap = rows;
     L.pub.m_align = kMAlign;
-    L.pub.n_part = (int32_t)(I / 64);
+    L.pub.n_part = (int32_t)(I / 32);
     L.total = o;
     return L;
 }
@@ -92,14 +95,19 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_E_HIP; }
 
-int grid_waves(int64_t tiles_bound) {
+// Persistent GEMM grid: two 4-wave workgroups per CU, at most one per tile.
+int grid_blocks(int64_t tiles_bound) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
         int v = 0;
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
-    const int64_t cap = (int64_t)cus * 4;  // one 512-register wave per SIMD
-    return (int)std::max<int64_t>(8, std::min<int64_t>(tiles_bound, cap));
+    return (int)std::max<int64_t>(8, std::min<int64_t>(tiles_bound, 2 * (int64_t)cus));
+}
+
+int32_t col_tiles(int64_t n, int mode) {
+    const int64_t w = gemm_cols_per_tile(mode);
+    return (int32_t)((n + w - 1) / w);
 }
 
 }  // namespace
@@ -131,7 +139,8 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, ui
     if (rows >= ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
     if (rows == 0) return NVFP4_OK;
     if (!x || !codes || !scales || !g) return NVFP4_E_NULL;
-    if (!aligned(x, 16) || ld % 8 != 0 || !aligned(codes, 4) || !aligned(g, 4)) return NVFP4_E_ALIGN;
+    if (!aligned(x, 16) || ld % 8 != 0 || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(g, 4))
+        return NVFP4_E_ALIGN;
     return hip_status(launch_quant_rows(x, rows, cols, ld, codes, scales, g, layout == NVFP4_LAYOUT_GEMM,
                                         scale_round == NVFP4_SCALE_RU, (hipStream_t)stream));
 }
@@ -211,13 +220,16 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     rb.pair2row = (int32_t*)(ws + L.pub.pair2row);
     rb.row2pair = (int32_t*)(ws + L.pub.row2pair);
     rb.row_prob = (float*)(ws + L.row_prob);
+    rb.xq_codes = ws + L.xq_codes;
+    rb.xq_scales = ws + L.xq_scales;
+    rb.gx = (float*)(ws + L.gx);
     rb.a_codes = ws + L.pub.a1_codes;
     rb.a_scales = ws + L.pub.a1_scales;
     rb.a_g = (float*)(ws + L.pub.a1_g);
     const bool ru = cfg->scale_round == NVFP4_SCALE_RU;
 
     if (!mark(0)) return NVFP4_E_HIP;
-    hipError_t e = launch_route(x, ids, probs, T, (int32_t)H, (int32_t)K, (int32_t)E, ru, rb, s);
+    hipError_t e = launch_route(x, ids, probs, T, (int32_t)H, (int32_t)K, (int32_t)E, ru, rb, L.pub.rows_cap, s);
     if (e != hipSuccess || !mark(1)) return NVFP4_E_HIP;
 
     // Static bound on row tiles for this T (the device count is <= this).
@@ -232,7 +244,7 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     f1.b_g = W1q->g;
     f1.K = (int32_t)H;
     f1.N = (int32_t)(2 * I);
-    f1.n_tiles_n = (int32_t)(I / 64);
+    f1.n_tiles_n = col_tiles(I, kGemmSwiGLU);
     f1.mtiles = rb.mtiles;
     f1.n_mtiles = rb.n_mtiles;
     f1.dense_m = -1;
@@ -240,14 +252,18 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     f1.ld_out = I;
     f1.row_prob = rb.row_prob;
     f1.amax_part = (float*)(ws + L.pub.amax2_part);
+    f1.n_part = (int32_t)(I / 32);
     f1.inter = (int32_t)I;
-    e = launch_gemm(kGemmSwiGLU, f1, grid_waves(mt_bound * f1.n_tiles_n), s);
+    e = launch_gemm(kGemmSwiGLU, f1, grid_blocks(mt_bound * f1.n_tiles_n), s);
     if (e != hipSuccess || !mark(2)) return NVFP4_E_HIP;
 
     uint8_t* a2c = ws + L.pub.a2_codes;
     uint8_t* a2s = ws + L.pub.a2_scales;
     float* a2g = (float*)(ws + L.pub.a2_g);
-    e = launch_quant_h(f1.out, (int64_t)T * K, I, rb.pair2row, f1.amax_part, f1.n_tiles_n, a2c, a2s, a2g, ru, s);
+    const int64_t rows_bound =
+        std::min<int64_t>(L.pub.rows_cap, ((int64_t)T * K + E * (kMAlign - 1) + kMAlign - 1) / kMAlign * kMAlign);
+    e = launch_quant_h(f1.out, rows_bound, I, rb.expert_off, (int32_t)E, rb.row2pair, f1.amax_part, f1.n_part, a2c,
+                       a2s, a2g, ru, s);
     if (e != hipSuccess || !mark(3)) return NVFP4_E_HIP;
 
     GemmParams f2{};
@@ -259,13 +275,13 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     f2.b_g = W2q->g;
     f2.K = (int32_t)I;
     f2.N = (int32_t)H;
-    f2.n_tiles_n = (int32_t)(H / 128);
+    f2.n_tiles_n = col_tiles(H, kGemmPlain);
     f2.mtiles = rb.mtiles;
     f2.n_mtiles = rb.n_mtiles;
     f2.dense_m = -1;
     f2.out = (uint16_t*)(ws + L.pub.y2);
     f2.ld_out = H;
-    e = launch_gemm(kGemmPlain, f2, grid_waves(mt_bound * f2.n_tiles_n), s);
+    e = launch_gemm(kGemmPlain, f2, grid_blocks(mt_bound * f2.n_tiles_n), s);
     if (e != hipSuccess || !mark(4)) return NVFP4_E_HIP;
 
     e = launch_combine(f2.out, rb.pair2row, T, (int32_t)H, (int32_t)K, out, s);
@@ -343,12 +359,12 @@ int nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const nvfp4_qtensor* W
     p.b_g = Wq->g;
     p.K = (int32_t)K;
     p.N = Wq->rows;
-    p.n_tiles_n = Wq->rows / 128;
+    p.n_tiles_n = col_tiles(Wq->rows, kGemmPlain);
     p.dense_m = (int32_t)M;
     p.out = out;
     p.ld_out = Wq->rows;
     const int64_t tiles = (M + kTileRows - 1) / kTileRows * p.n_tiles_n;
-    return hip_status(launch_gemm(kGemmPlain, p, grid_waves(tiles), s));
+    return hip_status(launch_gemm(kGemmPlain, p, grid_blocks(tiles), s));
 }
 
 }  // extern "C"

@@ -17,19 +17,28 @@
 //    conversion (v_cvt_scalef32_pk_f16_fp4) applies only the exponent of its
 //    scale operand, so it runs with scale 1.0 and the E4M3 block scale is
 //    applied by one packed f16 multiply (exact).
-//  * Operands go from HBM/L2 straight to registers: in the GEMM layout one
-//    16-byte load per lane fetches 32 rows x 64 columns contiguously, and a
-//    lane's 32 codes feed four MFMAs.  Both operands use the same column
-//    permutation inside a 64-column chunk, so the dot product is unchanged.
-//  * One wavefront per workgroup owns a 128 x 128 output tile (4 x 4 MFMA
-//    tiles, 256 FP32 accumulators): decode work per MFMA is halved relative
-//    to 64-wide tiles, which keeps the VALU decode inside the MFMA shadow.
-//  * Persistent waves walk a tile list whose length is read on the device (no
-//    host sync).  Waves with blockIdx % 8 == x (the same XCD under round-robin
-//    dispatch) take one contiguous range of tiles, so an expert's weight slab
-//    is fetched from HBM into that XCD's L2 once and reused by its row tiles.
-//  * No split-K, one K order, one instruction sequence per row for every
-//    batch size: a row's bits depend only on its own inputs.
+//  * A workgroup of 4 wavefronts (one per SIMD; two workgroups share each CU,
+//    so every SIMD runs two independent waves at 256 registers each) owns a
+//    tile of 128 rows x 256 B-rows (FC2: 256 output columns; FC1: 128 gate
+//    and the matching 128 up rows, i.e. 128 columns of h).  Each wave owns 128
+//    rows x 2 MFMA column tiles (128 FP32 accumulators).  The two workgroups
+//    on a CU drift apart, so one's epilogue and barriers overlap the other's
+//    MFMAs.
+//  * The activation tile is decoded once per workgroup: for every 128-column
+//    step wave w decodes the 32-row tile w (both 64-column chunks) into LDS,
+//    and all four waves read their MFMA A operands from there.  Each wave
+//    decodes its own weight columns in registers.  In the GEMM layout one
+//    16-byte load per lane fetches 32 rows x 64 columns as one contiguous
+//    1 KiB; both operands use the same column permutation inside a 64-column
+//    chunk, which leaves the dot product unchanged.
+//  * Double-buffered LDS, one barrier per 128-column step; loads for the next
+//    step are issued before the current step's MFMAs.
+//  * Persistent workgroups walk a tile list whose length is read on the device
+//    (no host sync).  Workgroups with blockIdx % 8 == x (one XCD under
+//    round-robin dispatch) take one contiguous range of tiles, so an expert's
+//    weight slab and its row tiles meet in that XCD's L2.
+//  * No split-K, one K order, one instruction sequence per row for every batch
+//    size: a row's bits depend only on its own inputs.
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
@@ -49,152 +58,221 @@ __device__ __forceinline__ half2v scale2(uint32_t sdw) {
     return half2v{s, s};
 }
 
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
+// Scale of k-steps {0,1} (first) and {2,3} (second) of chunk CH of a 128-column step.
+template <int CH>
+__device__ __forceinline__ void scales_of(uint32_t sdw, half2v& lo, half2v& hi) {
+    lo = scale2<2 * CH>(sdw);
+    hi = scale2<2 * CH + 1>(sdw);
+}
+
+// float -> BF16 bits with the hardware conversion (round to nearest even).
+__device__ __forceinline__ uint32_t bf16_hw(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// silu(a) = a / (1 + e^-a), with the hardware exp2 and reciprocal.
+__device__ __forceinline__ float silu_fast(float a) {
+    const float e = __builtin_amdgcn_exp2f(a * -1.4426950408889634f);
+    return a * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Max of an unsigned value over each 32-lane half of the wavefront: DPP within
+// 16-lane rows (quad swaps, then rotations by 4 and 8), a swizzle across rows.
+__device__ __forceinline__ uint32_t half_wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+    v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));                     // lane ^ 16
+    return v;
+}
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+
+// LDS: decoded A operands, [buffer][32-row tile][chunk][k-step][lane] x 16 bytes.
+struct SharedA {
+    half8 a[2][4][2][4][64];
+};
 
 template <int MODE, int NSUB>
-__device__ __forceinline__ void gemm_tile(const GemmParams& P, int32_t row0, int32_t expert, int32_t row_end,
-                                          int32_t nt) {
-    const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, int32_t row0, int32_t expert,
+                                           int32_t row_end, int32_t nt) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t K = P.K;
     const int64_t kc64 = K >> 6, kc128 = K >> 7;
-    // Row tiles (32 rows each) of A and B.
-    int64_t rta[NSUB], rtb[4];
-    int32_t bcol0[4];
-#pragma unroll
-    for (int i = 0; i < NSUB; i++) rta[i] = (row0 >> 5) + i;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        bcol0[j] = MODE == kGemmSwiGLU ? nt * 64 + 32 * (j & 1) + (j >> 1) * P.inter : nt * 128 + 32 * j;
-        rtb[j] = ((int64_t)expert * P.N + bcol0[j]) >> 5;
+
+    // This wave's two weight column tiles.
+    int32_t bcol0[2];
+    bool active;
+    if (MODE == kGemmSwiGLU) {
+        const int32_t hc = nt * 128 + 32 * wave;
+        active = hc < P.inter;
+        bcol0[0] = hc;            // gate rows
+        bcol0[1] = P.inter + hc;  // the matching up rows
+    } else {
+        const int32_t c = nt * 256 + 64 * wave;
+        active = c < P.N;
+        bcol0[0] = c;
+        bcol0[1] = c + 32;
     }
+    int64_t rtb[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) rtb[j] = ((int64_t)expert * P.N + bcol0[j]) >> 5;
+
+    // The activation units this wave decodes for every 128-column step: its
+    // 32-row tile `wave`, both 64-column chunks.
+    const int ai = wave;
+    const bool adec = ai < NSUB;
+    const int64_t rta = (row0 >> 5) + ai;
+
     const uint8_t* a_c = P.a_codes + lane * 16;
-    const uint8_t* b_c = P.b_codes + lane * 16;
     const uint8_t* a_s = P.a_scales + lane * 4;
+    const uint8_t* b_c = P.b_codes + lane * 16;
     const uint8_t* b_s = P.b_scales + lane * 4;
 
-    f32x16 acc[NSUB][4];
+    f32x16 acc[NSUB][2];
 #pragma unroll
-    for (int i = 0; i < NSUB; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = f32x16{};
+    for (int i = 0; i < NSUB; i++) {
+        acc[i][0] = f32x16{};
+        acc[i][1] = f32x16{};
+    }
 
-    // Raw operands for one 128-column step (two 64-column chunks).
-    u32x4 ca[2][NSUB], cb[2][4];
-    uint32_t sa[NSUB], sb[4];
-    auto load = [&](int64_t cp, u32x4 (&xa)[2][NSUB], u32x4 (&xb)[2][4], uint32_t (&ya)[NSUB],
-                    uint32_t (&yb)[4]) {
+    u32x4 ua[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    uint32_t usa = 0u;
+    u32x4 ub[2][2];  // [chunk][column tile]
+    uint32_t usb[2] = {0u, 0u};
+    auto load = [&](int64_t cp, u32x4 (&xa)[2], uint32_t& ya, u32x4 (&xb)[2][2], uint32_t (&yb)[2]) {
+        if (adec) {
 #pragma unroll
-        for (int ch = 0; ch < 2; ch++) {
-#pragma unroll
-            for (int i = 0; i < NSUB; i++)
-                xa[ch][i] = *reinterpret_cast<const u32x4*>(a_c + (rta[i] * kc64 + 2 * cp + ch) * 1024);
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                xb[ch][j] = *reinterpret_cast<const u32x4*>(b_c + (rtb[j] * kc64 + 2 * cp + ch) * 1024);
+            for (int ch = 0; ch < 2; ch++)
+                xa[ch] = *reinterpret_cast<const u32x4*>(a_c + (rta * kc64 + 2 * cp + ch) * 1024);
+            ya = *reinterpret_cast<const uint32_t*>(a_s + (rta * kc128 + cp) * 256);
         }
+        if (active) {
 #pragma unroll
-        for (int i = 0; i < NSUB; i++) ya[i] = *reinterpret_cast<const uint32_t*>(a_s + (rta[i] * kc128 + cp) * 256);
+            for (int ch = 0; ch < 2; ch++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) yb[j] = *reinterpret_cast<const uint32_t*>(b_s + (rtb[j] * kc128 + cp) * 256);
+                for (int j = 0; j < 2; j++)
+                    xb[ch][j] = *reinterpret_cast<const u32x4*>(b_c + (rtb[j] * kc64 + 2 * cp + ch) * 1024);
+#pragma unroll
+            for (int j = 0; j < 2; j++) yb[j] = *reinterpret_cast<const uint32_t*>(b_s + (rtb[j] * kc128 + cp) * 256);
+        }
+    };
+    auto decode_a = [&](int buf, const u32x4 (&xa)[2], uint32_t ya) {
+        if (!adec) return;
+        half2v lo0, hi0, lo1, hi1;
+        scales_of<0>(ya, lo0, hi0);
+        scales_of<1>(ya, lo1, hi1);
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) S.a[buf][ai][0][ks][lane] = decode8(xa[0][ks], ks < 2 ? lo0 : hi0);
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) S.a[buf][ai][1][ks][lane] = decode8(xa[1][ks], ks < 2 ? lo1 : hi1);
     };
 
-    load(0, ca, cb, sa, sb);
+    load(0, ua, usa, ub, usb);
+    decode_a(0, ua, usa);
+    __syncthreads();
     for (int64_t cp = 0; cp < kc128; cp++) {
-        u32x4 na[2][NSUB], nb[2][4];
-        uint32_t nsa[NSUB], nsb[4];
-        if (cp + 1 < kc128) load(cp + 1, na, nb, nsa, nsb);
+        const int buf = (int)(cp & 1);
+        u32x4 na[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+        uint32_t nsa = 0u;
+        u32x4 nb[2][2];
+        uint32_t nsb[2] = {0u, 0u};
+        const bool more = cp + 1 < kc128;
+        if (more) load(cp + 1, na, nsa, nb, nsb);
+        if (active) {
+            // Eight k-steps of 16 columns; the A operands of step s+1 are read from
+            // LDS while the MFMAs of step s run.
+            half2v bsc[2][2][2];  // [chunk][column tile][lo/hi]
 #pragma unroll
-        for (int ch = 0; ch < 2; ch++) {
-            // scale of the block holding k-steps 0,1 (sel ch*2) and 2,3 (sel ch*2+1) of this chunk
-            half2v as0[NSUB], as1[NSUB], bs0[4], bs1[4];
-#pragma unroll
-            for (int i = 0; i < NSUB; i++) {
-                as0[i] = ch == 0 ? scale2<0>(sa[i]) : scale2<2>(sa[i]);
-                as1[i] = ch == 0 ? scale2<1>(sa[i]) : scale2<3>(sa[i]);
+            for (int j = 0; j < 2; j++) {
+                scales_of<0>(usb[j], bsc[0][j][0], bsc[0][j][1]);
+                scales_of<1>(usb[j], bsc[1][j][0], bsc[1][j][1]);
             }
+            half8 acur[NSUB];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                bs0[j] = ch == 0 ? scale2<0>(sb[j]) : scale2<2>(sb[j]);
-                bs1[j] = ch == 0 ? scale2<1>(sb[j]) : scale2<3>(sb[j]);
-            }
+            for (int i = 0; i < NSUB; i++) acur[i] = S.a[buf][i][0][0][lane];
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++) {
-                half8 av[NSUB], bv[4];
+            for (int st = 0; st < 8; st++) {
+                const int ch = st >> 2, ks = st & 3;
+                half8 anxt[NSUB];
+                if (st < 7) {
 #pragma unroll
-                for (int i = 0; i < NSUB; i++) av[i] = decode8(ca[ch][i][ks], ks < 2 ? as0[i] : as1[i]);
+                    for (int i = 0; i < NSUB; i++) anxt[i] = S.a[buf][i][(st + 1) >> 2][(st + 1) & 3][lane];
+                }
+                half8 bv[2];
 #pragma unroll
-                for (int j = 0; j < 4; j++) bv[j] = decode8(cb[ch][j][ks], ks < 2 ? bs0[j] : bs1[j]);
+                for (int j = 0; j < 2; j++) bv[j] = decode8(ub[ch][j][ks], bsc[ch][j][ks >> 1]);
 #pragma unroll
                 for (int i = 0; i < NSUB; i++)
 #pragma unroll
-                    for (int j = 0; j < 4; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < 2; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(acur[i], bv[j], acc[i][j], 0, 0, 0);
+                if (st < 7) {
+#pragma unroll
+                    for (int i = 0; i < NSUB; i++) acur[i] = anxt[i];
+                }
             }
         }
-        if (cp + 1 < kc128) {
+        if (more) {
+            decode_a(buf ^ 1, na, nsa);
 #pragma unroll
-            for (int ch = 0; ch < 2; ch++) {
+            for (int ch = 0; ch < 2; ch++)
 #pragma unroll
-                for (int i = 0; i < NSUB; i++) ca[ch][i] = na[ch][i];
-#pragma unroll
-                for (int j = 0; j < 4; j++) cb[ch][j] = nb[ch][j];
-            }
-#pragma unroll
-            for (int i = 0; i < NSUB; i++) sa[i] = nsa[i];
-#pragma unroll
-            for (int j = 0; j < 4; j++) sb[j] = nsb[j];
+                for (int j = 0; j < 2; j++) ub[ch][j] = nb[ch][j];
+            usb[0] = nsb[0];
+            usb[1] = nsb[1];
         }
+        __syncthreads();
     }
+    if (!active) return;
 
     // Epilogue.  Lane l holds, for register r of an MFMA tile, row
-    // (r/4)*8 + (l/32)*4 + r%4 and column l%32 of that 32x32 tile.
+    // (r/4)*8 + (l/32)*4 + r%4 and column l%32 of that 32x32 tile.  Row
+    // pointers are uniform per register (scalar address math); only the
+    // half-wave row offset and the column are per lane.
     const int colL = lane & 31;
     const int rowL = (lane >> 5) * 4;
     if (MODE == kGemmSwiGLU) {
-        const float gwg0 = P.b_g[(int64_t)expert * P.N + bcol0[0] + colL];
-        const float gwg1 = P.b_g[(int64_t)expert * P.N + bcol0[1] + colL];
-        const float gwu0 = P.b_g[(int64_t)expert * P.N + bcol0[2] + colL];
-        const float gwu1 = P.b_g[(int64_t)expert * P.N + bcol0[3] + colL];
+        const float gwg = P.b_g[(int64_t)expert * P.N + bcol0[0] + colL];
+        const float gwu = P.b_g[(int64_t)expert * P.N + bcol0[1] + colL];
+        const int64_t lane_off = (int64_t)rowL * P.ld_out + bcol0[0] + colL;
+        const int32_t part = bcol0[0] >> 5;
 #pragma unroll
         for (int i = 0; i < NSUB; i++) {
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int32_t row = row0 + 32 * i + (r >> 2) * 8 + rowL + (r & 3);
-                const bool valid = row < row_end;
+                const int32_t rowu = row0 + 32 * i + (r >> 2) * 8 + (r & 3);  // uniform
+                const int32_t row = rowu + rowL;
+                const bool valid = row < row_end;  // uniform within each half-wave
                 const float gx = valid ? P.a_g[row] : 0.0f;
                 const float pr = valid ? P.row_prob[row] : 0.0f;
-                float m = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const float gg = gx * (j == 0 ? gwg0 : gwg1);
-                    const float gu = gx * (j == 0 ? gwu0 : gwu1);
-                    const float yg = bf16_to_f32(f32_to_bf16_rne(acc[i][j][r] * gg));
-                    const float yu = bf16_to_f32(f32_to_bf16_rne(acc[i][j + 2][r] * gu));
-                    const uint32_t hb = f32_to_bf16_rne(silu(yg) * yu * pr);
-                    m = fmaxf(m, fabsf(bf16_to_f32(hb)));
-                    if (valid) P.out[(int64_t)row * P.ld_out + nt * 64 + 32 * j + colL] = (uint16_t)hb;
+                const float yg = bf16_to_f32(bf16_hw(acc[i][0][r] * (gx * gwg)));
+                const float yu = bf16_to_f32(bf16_hw(acc[i][1][r] * (gx * gwu)));
+                const uint32_t hb = bf16_hw(silu_fast(yg) * yu * pr);
+                // max |h| over the wave's 32 columns of this row: the BF16 bit
+                // patterns of |h| order like their values, so integer max is exact.
+                const uint32_t m = half_wave_max_u32(hb & 0x7FFFu);
+                if (valid) {
+                    P.out[(int64_t)rowu * P.ld_out + lane_off] = (uint16_t)hb;
+                    if (colL == 0) P.amax_part[(int64_t)row * P.n_part + part] = __uint_as_float(m << 16);
                 }
-#pragma unroll
-                for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-                if (valid && colL == 0) P.amax_part[(int64_t)row * P.n_tiles_n + nt] = m;
             }
         }
     } else {
-        float gw[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) gw[j] = P.b_g[(int64_t)expert * P.N + bcol0[j] + colL];
+        const float gw0 = P.b_g[(int64_t)expert * P.N + bcol0[0] + colL];
+        const float gw1 = P.b_g[(int64_t)expert * P.N + bcol0[1] + colL];
+        const int64_t lane_off = (int64_t)rowL * P.ld_out + bcol0[0] + colL;
 #pragma unroll
         for (int i = 0; i < NSUB; i++) {
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int32_t row = row0 + 32 * i + (r >> 2) * 8 + rowL + (r & 3);
+                const int32_t rowu = row0 + 32 * i + (r >> 2) * 8 + (r & 3);  // uniform
+                const int32_t row = rowu + rowL;
                 if (row < row_end) {
                     const float ga = P.a_g[row];
-#pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        const uint32_t y = f32_to_bf16_rne(acc[i][j][r] * (ga * gw[j]));
-                        P.out[(int64_t)row * P.ld_out + bcol0[j] + colL] = (uint16_t)y;
-                    }
+                    uint16_t* o = P.out + (int64_t)rowu * P.ld_out + lane_off;
+                    o[0] = (uint16_t)bf16_hw(acc[i][0][r] * (ga * gw0));
+                    o[32] = (uint16_t)bf16_hw(acc[i][1][r] * (ga * gw1));
                 }
             }
         }
@@ -202,12 +280,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, int32_t row0, int
 }
 
 template <int MODE>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_kernel(GemmParams P) {
+    __shared__ SharedA S;
     const int64_t n_mt = P.dense_m >= 0 ? (P.dense_m + kTileRows - 1) / kTileRows : *P.n_mtiles;
     const int64_t total = n_mt * P.n_tiles_n;
-    const int64_t nw = gridDim.x;          // a multiple of 8
-    const int64_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = nw >> 3;
+    const int64_t nb = gridDim.x;  // a multiple of 8
+    const int64_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = nb >> 3;
     const int64_t t_begin = total * xcd / 8, t_end = total * (xcd + 1) / 8;
     for (int64_t t = t_begin + slot; t < t_end; t += per) {
         const int64_t mt = t / P.n_tiles_n;
@@ -226,20 +305,23 @@ gemm_kernel(GemmParams P) {
             row_end = d.w;
         }
         switch (nsub) {
-            case 4: gemm_tile<MODE, 4>(P, row0, expert, row_end, nt); break;
-            case 3: gemm_tile<MODE, 3>(P, row0, expert, row_end, nt); break;
-            case 2: gemm_tile<MODE, 2>(P, row0, expert, row_end, nt); break;
-            default: gemm_tile<MODE, 1>(P, row0, expert, row_end, nt); break;
+            case 4: block_tile<MODE, 4>(P, S, row0, expert, row_end, nt); break;
+            case 3: block_tile<MODE, 3>(P, S, row0, expert, row_end, nt); break;
+            case 2: block_tile<MODE, 2>(P, S, row0, expert, row_end, nt); break;
+            default: block_tile<MODE, 1>(P, S, row0, expert, row_end, nt); break;
         }
+        __syncthreads();  // the next tile's prologue overwrites LDS buffer 0
     }
 }
 
-hipError_t launch_gemm(int mode, const GemmParams& P, int grid_waves, hipStream_t stream) {
-    const int g = (grid_waves + 7) / 8 * 8;
+int gemm_cols_per_tile(int mode) { return mode == kGemmSwiGLU ? 128 : 256; }
+
+hipError_t launch_gemm(int mode, const GemmParams& P, int grid_blocks, hipStream_t stream) {
+    const int g = (grid_blocks + 7) / 8 * 8;
     if (mode == kGemmSwiGLU)
-        hipLaunchKernelGGL(gemm_kernel<kGemmSwiGLU>, dim3(g), dim3(64), 0, stream, P);
+        hipLaunchKernelGGL(gemm_kernel<kGemmSwiGLU>, dim3(g), dim3(kThreads), 0, stream, P);
     else
-        hipLaunchKernelGGL(gemm_kernel<kGemmPlain>, dim3(g), dim3(64), 0, stream, P);
+        hipLaunchKernelGGL(gemm_kernel<kGemmPlain>, dim3(g), dim3(kThreads), 0, stream, P);
     return hipGetLastError();
 }
 

@@ -30,7 +30,8 @@ struct GemmParams {
     uint16_t* out;
     int64_t ld_out;
     const float* row_prob;     // SwiGLU mode: router probability per row
-    float* amax_part;          // SwiGLU mode: [rows][n_tiles_n] max |h|
+    float* amax_part;          // SwiGLU mode: [rows][n_part] max |h| of each 32-column group
+    int32_t n_part;            // SwiGLU mode: I / 32
     int32_t inter;             // SwiGLU mode: I (gate rows [0, I), up rows [I, 2I))
 };
 
@@ -45,18 +46,23 @@ struct RouteBuffers {
     int32_t* pair2row;     // [T*K]
     int32_t* row2pair;     // [rows_cap]
     float* row_prob;       // [rows_cap]
-    uint8_t* a_codes;
+    uint8_t* xq_codes;     // [T][H/2] token-major quantized X (logical layout)
+    uint8_t* xq_scales;    // [T][H/16]
+    float* gx;             // [T]
+    uint8_t* a_codes;      // sorted, padded A1 (GEMM layout)
     uint8_t* a_scales;
     float* a_g;
 };
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
                              uint8_t* scales, float* g, bool gemm, bool round_up, hipStream_t stream);
-hipError_t launch_quant_h(const uint16_t* h, int64_t P, int64_t I, const int32_t* pair2row, const float* amax2_part,
-                          int n_part, uint8_t* codes, uint8_t* scales, float* g, bool round_up, hipStream_t stream);
+hipError_t launch_quant_h(const uint16_t* h, int64_t rows_bound, int64_t I, const int32_t* expert_off, int32_t E,
+                          const int32_t* row2pair, const float* amax2_part, int n_part, uint8_t* codes,
+                          uint8_t* scales, float* g, bool round_up, hipStream_t stream);
 hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* probs, int32_t T, int32_t H, int32_t K,
-                        int32_t E, bool round_up, const RouteBuffers& rb, hipStream_t stream);
-hipError_t launch_gemm(int mode, const GemmParams& P, int grid_waves, hipStream_t stream);
+                        int32_t E, bool round_up, const RouteBuffers& rb, int64_t rows_cap, hipStream_t stream);
+int gemm_cols_per_tile(int mode);  // output columns per tile: 256 (plain) or 128 of h (128 gate + 128 up rows)
+hipError_t launch_gemm(int mode, const GemmParams& P, int grid_blocks, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* y2, const int32_t* pair2row, int32_t T, int32_t H, int32_t K,
                           uint16_t* out, hipStream_t stream);
 

@@ -1,45 +1,67 @@
-// quant.hip -- NVFP4 row quantizer on gfx950.
+// quant.hip -- NVFP4 quantizers on gfx950.
 //
 // miniTE summary page, "how it differs": per-row FP32 outer scale
 // g = max|row| / (6*448), one E4M3 scale per 16 elements, E2M1 codes, round
-// to nearest, no Hadamard transform, no stochastic rounding.  One wavefront
-// owns one row: the row amax is a wave reduction, each lane then quantizes
-// 8-element groups (a 16-element block spans two neighbouring lanes, whose
-// maxima meet in one shuffle).  Loads are 16 B per lane, so a wave reads 1 KiB
-// contiguous per step; HBM-bound.
+// to nearest, no Hadamard transform, no stochastic rounding.  Both kernels are
+// HBM-bound streaming kernels: each lane reads 64 contiguous bytes of one row
+// and writes 16 bytes of codes.
+//   quant_rows_kernel  one wave per row (generic entry point, weights, dense X);
+//   quant_h_kernel     FC2 input: one wave per (32-row tile, 128 columns) of
+//                      the sorted buffer, writing whole 1 KiB GEMM chunks; the
+//                      row amax is the max of the per-32-column maxima the FC1
+//                      producer emitted (miniTE page, "how to use it": FC2
+//                      maxima come from the router-weighted producer).
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 #include "nvfp4_quant_row.h"
 
 namespace nvfp4 {
 
-// Generic quantizer: one wave per row, four rows per 256-thread block.
 __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                          int64_t ld, uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ scales, float* __restrict__ g,
                                                          int gemm, int round_up) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
-    int64_t dst = row;
-    quant_row_wave(x + row * ld, cols, -1.0f, round_up != 0, gemm != 0, &dst, 1, codes, scales, g);
+    quant_row_wave(x + row * ld, cols, -1.0f, round_up != 0, gemm != 0, row, codes, scales, g);
 }
 
-// FC2 input: quantize h of every (token, slot) pair.  The row amax is the max
-// of the per-column-tile maxima the FC1 producer emitted for this row (the
-// maxima of the tensor FC2 actually consumes, miniTE page "how to use it").
-__global__ void __launch_bounds__(256) quant_h_kernel(const uint16_t* __restrict__ h, int64_t P, int64_t I,
-                                                      const int32_t* __restrict__ pair2row,
+__global__ void __launch_bounds__(256) quant_h_kernel(const uint16_t* __restrict__ h, int64_t I,
+                                                      const int32_t* __restrict__ expert_off, int32_t E,
+                                                      const int32_t* __restrict__ row2pair,
                                                       const float* __restrict__ amax2_part, int n_part,
-                                                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                      float* __restrict__ g, int round_up) {
-    const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (p >= P) return;
-    const int32_t row = pair2row[p];
-    if (row < 0) return;
+                                                      int64_t n_units, uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales, float* __restrict__ g,
+                                                      int round_up) {
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (unit >= n_units) return;
+    const int64_t cps = I / 128;
+    const int64_t rt = unit / cps, cp = unit % cps;
+    if (rt * 32 >= expert_off[E]) return;  // past the last expert's rows
+    const int hh = lane >> 5, rl = lane & 31;
+    const int64_t row = rt * 32 + rl;
+    const bool valid = row2pair[row] >= 0;  // padding rows are written as zeros
     float amax = 0.0f;
-    for (int i = 0; i < n_part; i++) amax = fmaxf(amax, amax2_part[(int64_t)row * n_part + i]);
-    int64_t dst = row;
-    quant_row_wave(h + (int64_t)row * I, I, amax, round_up != 0, true, &dst, 1, codes, scales, g);
+    if (valid)
+        for (int i = 0; i < n_part; i++) amax = fmaxf(amax, amax2_part[row * n_part + i]);
+    const RowScale rs = row_scale(amax);
+    uint32_t sc = 0u;
+#pragma unroll
+    for (int ch = 0; ch < 2; ch++) {
+        const int64_t c = 2 * cp + ch;
+        u32x4 cw = {0u, 0u, 0u, 0u};
+        uint32_t s2 = 0u;
+        if (valid) {
+            u32x4 v[4];
+            load32(h + row * I + 64 * c + 32 * hh, false, v);
+            quant32(v, rs, round_up != 0, false, cw, s2);
+        }
+        *reinterpret_cast<u32x4*>(codes + (rt * (I / 64) + c) * 1024 + lane * 16) = cw;
+        sc |= s2 << (16 * ch);
+    }
+    *reinterpret_cast<uint32_t*>(scales + (rt * (I / 128) + cp) * 256 + lane * 4) = sc;
+    if (cp == 0 && hh == 0) g[row] = valid ? rs.g : 0.0f;
 }
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
@@ -51,12 +73,13 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
     return hipGetLastError();
 }
 
-hipError_t launch_quant_h(const uint16_t* h, int64_t P, int64_t I, const int32_t* pair2row, const float* amax2_part,
-                          int n_part, uint8_t* codes, uint8_t* scales, float* g, bool round_up, hipStream_t stream) {
-    if (P <= 0) return hipSuccess;
-    const int64_t blocks = (P + 3) / 4;
-    hipLaunchKernelGGL(quant_h_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, h, P, I, pair2row, amax2_part,
-                       n_part, codes, scales, g, round_up ? 1 : 0);
+hipError_t launch_quant_h(const uint16_t* h, int64_t rows_bound, int64_t I, const int32_t* expert_off, int32_t E,
+                          const int32_t* row2pair, const float* amax2_part, int n_part, uint8_t* codes,
+                          uint8_t* scales, float* g, bool round_up, hipStream_t stream) {
+    const int64_t n_units = rows_bound / 32 * (I / 128);
+    if (n_units <= 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_h_kernel, dim3((unsigned)((n_units + 3) / 4)), dim3(256), 0, stream, h, I, expert_off, E,
+                       row2pair, amax2_part, n_part, n_units, codes, scales, g, round_up ? 1 : 0);
     return hipGetLastError();
 }
 

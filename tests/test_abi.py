@@ -58,7 +58,7 @@ def test_workspace_bytes_depend_on_config_only(m):
     assert a > 0 and a % 256 == 0
     assert m.workspace_bytes(_cfg(m, max_tokens=8192)) > a
     lay = m.workspace_layout(_cfg(m))
-    assert lay.m_align == 32 and lay.n_part == 768 // 64
+    assert lay.m_align == 32 and lay.n_part == 768 // 32
     assert lay.rows_cap >= 4096 * 8 + 128 * 31 and lay.rows_cap % 32 == 0
     offs = [lay.err, lay.expert_count, lay.expert_off, lay.pair2row, lay.row2pair, lay.a1_codes, lay.a1_scales,
             lay.a1_g, lay.h, lay.amax2_part, lay.a2_codes, lay.a2_scales, lay.a2_g, lay.y2]

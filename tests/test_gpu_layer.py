@@ -111,7 +111,7 @@ def _stage_checks(orc, layer, x, ids, probs, out, mode):
     hv = np.abs(W.bf16_bits_to_f32(h))
     assert np.array_equal(part.max(axis=1), hv.max(axis=1)), "FC2 amax from the producer"
     for j in range(lay.n_part):
-        assert np.array_equal(part[:, j], hv[:, 64 * j:64 * (j + 1)].max(axis=1)), f"column tile {j} max"
+        assert np.array_equal(part[:, j], hv[:, 32 * j:32 * (j + 1)].max(axis=1)), f"column group {j} max"
     # A2 = Q(h) bit-exact, given the GPU's own h
     c = layer.ws_array(lay.a2_codes, np.uint8, rows * s.I // 2)
     sc = layer.ws_array(lay.a2_scales, np.uint8, rows * s.I // 16)
