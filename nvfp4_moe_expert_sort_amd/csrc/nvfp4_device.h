@@ -58,14 +58,6 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v, bool round_up) {
 // E4M3FN byte -> float (gfx950 converts the OCP E4M3FN format in hardware).
 __device__ __forceinline__ float e4m3_decode(uint32_t byte) { return __builtin_amdgcn_cvt_f32_fp8(byte, 0); }
 
-// E2M1 magnitude code of q >= 0: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6},
-// ties to the even code, saturating.  Each comparison is one decision
-// threshold; '>' at a tie keeps the lower (even) code, '>=' takes the upper.
-__device__ __forceinline__ uint32_t e2m1_magnitude(float q) {
-    return (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f) + (uint32_t)(q > 1.25f) + (uint32_t)(q >= 1.75f) +
-           (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) + (uint32_t)(q > 5.0f);
-}
-
 // --- GEMM layout (see include/nvfp4moe.h) -------------------------------------------------------
 // Byte offset of the 4-byte group holding columns [k, k+8) (k % 8 == 0) of row r.
 __device__ __forceinline__ size_t gemm_code_off(int64_t r, int64_t k, int64_t cols) {
@@ -82,6 +74,12 @@ __device__ __forceinline__ size_t gemm_scale_off(int64_t r, int64_t k, int64_t c
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
     return v;
 }
 

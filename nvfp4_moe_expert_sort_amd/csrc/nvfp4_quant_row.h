@@ -32,34 +32,75 @@ __device__ __forceinline__ RowScale row_scale(float amax) {
     return r;
 }
 
-// Max |x| over the 8 BF16 values packed in one u32x4.
-__device__ __forceinline__ float absmax8(u32x4 v) {
-    float m = 0.0f;
+// Max of |x| over the 8 BF16 values packed in one u32x4, as a BF16 bit
+// pattern: for finite values the bits of |x| order like the values, so the
+// integer max is exact.
+__device__ __forceinline__ uint32_t absmax8_bits(u32x4 v) {
+    uint32_t m = 0u;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        m = fmaxf(m, fabsf(bf16_to_f32(v[j] & 0xFFFFu)));
-        m = fmaxf(m, fabsf(bf16_to_f32(v[j] >> 16)));
-    }
+    for (int j = 0; j < 4; j++) m = max(m, max(v[j] & 0x7FFFu, (v[j] >> 16) & 0x7FFFu));
     return m;
+}
+
+__device__ __forceinline__ float absmax8(u32x4 v) { return bf16_to_f32(absmax8_bits(v)); }
+
+// fl32(a / b) from y = fl32(1 / b) with two FMAs (Markstein's correction
+// step).  Equal to the IEEE quotient for every binary32 b and every BF16 a
+// whose quotient lies in [2^-5, 2^5): checked exhaustively (all 2^23 divisor
+// significands x all BF16 dividend significands over that quotient range).
+// Quotients below 2^-5 or above 2^5 are far from every E2M1 decision
+// threshold (0.25 .. 5), so the code they give is the same either way.
+__device__ __forceinline__ float quot(float a, float b, float y) {
+    const float q0 = a * y;
+    const float r = __builtin_fmaf(-q0, b, a);
+    return __builtin_fmaf(r, y, q0);
+}
+
+// Two E2M1 codes into byte SEL of `old`: the hardware conversion
+// v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds to the nearest E2M1 value,
+// ties to the even code, saturating at 6, and keeps the sign bit.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t old, float q0, float q1) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, q0, q1, 1.0f, SEL);
+}
+
+// Signed quotient |x| / sg with x's sign bit (keeps -0), from a BF16 pattern.
+__device__ __forceinline__ float signed_q(uint32_t b, float sg, float y, bool fast) {
+    const float a = __uint_as_float((b & 0x7FFFu) << 16);
+    const float q = fast ? quot(a, sg, y) : a / sg;
+    return __uint_as_float(__float_as_uint(q) | ((b & 0x8000u) << 16));
 }
 
 // Quantize one 16-element block (two u32x4 of BF16 pairs) -> two code words and the scale byte.
 __device__ __forceinline__ void quant_block16(u32x4 lo, u32x4 hi, const RowScale& rs, bool round_up, uint32_t& w0,
                                               uint32_t& w1, uint32_t& sbyte) {
-    const float bmax = fmaxf(absmax8(lo), absmax8(hi));
+    const float bmax = bf16_to_f32(max(absmax8_bits(lo), absmax8_bits(hi)));
     sbyte = rs.zero ? 0u : e4m3_encode(bmax / rs.d, round_up);
     const float sg = e4m3_decode(sbyte) * rs.g;
-    uint32_t w[2] = {0u, 0u};
+    if (sg == 0.0f) {  // zero block or scale underflow: codes keep only the sign
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+            const u32x4 v = half ? hi : lo;
+#pragma unroll
+            for (int j = 0; j < 8; j++) w[half] |= (((v[j >> 1] >> (16 * (j & 1))) >> 15) & 1u) << (4 * j + 3);
+        }
+        w0 = w[0];
+        w1 = w[1];
+        return;
+    }
+    const float y = 1.0f / sg;                      // IEEE division, once per block
+    const bool fast = y < __builtin_huge_valf();   // a reciprocal that overflows (sg < 2^-128) takes the slow path
+    uint32_t w[2];
 #pragma unroll
     for (int half = 0; half < 2; half++) {
         const u32x4 v = half ? hi : lo;
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const uint32_t b = (v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-            uint32_t mag = 0u;
-            if (sg != 0.0f) mag = e2m1_magnitude(fabsf(bf16_to_f32(b)) / sg);
-            w[half] |= (((b >> 15) << 3) | mag) << (4 * j);
-        }
+        uint32_t acc = 0u;
+        acc = fp4_pair<0>(acc, signed_q(v[0] & 0xFFFFu, sg, y, fast), signed_q(v[0] >> 16, sg, y, fast));
+        acc = fp4_pair<1>(acc, signed_q(v[1] & 0xFFFFu, sg, y, fast), signed_q(v[1] >> 16, sg, y, fast));
+        acc = fp4_pair<2>(acc, signed_q(v[2] & 0xFFFFu, sg, y, fast), signed_q(v[2] >> 16, sg, y, fast));
+        acc = fp4_pair<3>(acc, signed_q(v[3] & 0xFFFFu, sg, y, fast), signed_q(v[3] >> 16, sg, y, fast));
+        w[half] = acc;
     }
     w0 = w[0];
     w1 = w[1];
@@ -99,14 +140,14 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ x, i
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t groups = (cols + 31) >> 5;  // 32-element groups; the last may hold one block
     if (amax < 0.0f) {
-        float m = 0.0f;
+        uint32_t m = 0u;
         for (int64_t gi = lane; gi < groups; gi += kWave) {
             const bool one = (gi + 1) * 32 > cols;
             u32x4 v[4];
             load32(x + gi * 32, one, v);
-            m = fmaxf(m, fmaxf(fmaxf(absmax8(v[0]), absmax8(v[1])), fmaxf(absmax8(v[2]), absmax8(v[3]))));
+            m = max(m, max(max(absmax8_bits(v[0]), absmax8_bits(v[1])), max(absmax8_bits(v[2]), absmax8_bits(v[3]))));
         }
-        amax = wave_max(m);
+        amax = bf16_to_f32(wave_max_u32(m));
     }
     const RowScale rs = row_scale(amax);
     for (int64_t gi = lane; gi < groups; gi += kWave) {

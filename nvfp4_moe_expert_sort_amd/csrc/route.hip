@@ -110,11 +110,12 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(int32_t nblk, int32_t 
     // (1) per-expert exclusive prefix over blocks: tpe threads per expert, each
     //     owning a contiguous segment of blocks; loads issued 8 at a time.
     const int tpe = 1024 / E;  // >= 1 since E <= 1024
-    const int e1 = tid / tpe, sub = tid % tpe;
+    const int e1 = tid % E, sub = tid / E;  // consecutive lanes read consecutive experts (coalesced)
+    // (threads with sub >= tpe own no segment)
     const int seg = (nblk + tpe - 1) / tpe;
-    const int b0 = min(sub * seg, nblk), b1 = min(b0 + seg, nblk);
+    const int b0 = min(sub * seg, nblk), b1 = sub < tpe ? min(b0 + seg, nblk) : b0;
     int32_t sum = 0;
-    if (e1 < E) {
+    if (sub < tpe) {
         int b = b0;
         for (; b + 8 <= b1; b += 8) {
             int32_t v[8];
@@ -125,12 +126,12 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(int32_t nblk, int32_t 
         }
         for (; b < b1; b++) sum += blk_counts[(int64_t)b * E + e1];
     }
-    part[tid] = sum;
+    if (sub < tpe) part[e1 * tpe + sub] = sum;
     int my_err = 0;
     for (int b = tid; b < nblk; b += 1024) my_err |= blk_err[b];
     if (my_err) atomicOr(&errs, my_err);
     __syncthreads();
-    if (e1 < E) {
+    if (sub < tpe) {
         int32_t run = 0;
         for (int s = 0; s < sub; s++) run += part[e1 * tpe + s];
         int b = b0;
