@@ -74,21 +74,13 @@ __device__ __forceinline__ float silu_fast(float a) {
     return a * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// Max of an unsigned value over each 32-lane half of the wavefront: DPP within
-// 16-lane rows (quad swaps, then rotations by 4 and 8), a swizzle across rows.
-__device__ __forceinline__ uint32_t half_wave_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
-    v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));                     // lane ^ 16
-    return v;
-}
-
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
 // LDS: decoded A operands, [buffer][32-row tile][chunk][k-step][lane] x 16 bytes.
+// After the K loop the same 64 KiB stage the epilogue (per-wave slices).
 struct SharedA {
     half8 a[2][4][2][4][64];
 };
@@ -227,54 +219,89 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, int3
     if (!active) return;
 
     // Epilogue.  Lane l holds, for register r of an MFMA tile, row
-    // (r/4)*8 + (l/32)*4 + r%4 and column l%32 of that 32x32 tile.  Row
-    // pointers are uniform per register (scalar address math); only the
-    // half-wave row offset and the column are per lane.
+    // (r/4)*8 + (l/32)*4 + r%4 and column l%32 of that 32x32 tile.  Results go
+    // through this wave's own slice of the (now idle) LDS operand buffers, so
+    // global stores are 16 bytes per lane and each row's max |h| is a
+    // lane-local reduction.  The slice is wave-private; the barrier at the end
+    // of the tile loop orders it against the next tile's LDS writes.
     const int colL = lane & 31;
     const int rowL = (lane >> 5) * 4;
     if (MODE == kGemmSwiGLU) {
+        constexpr int kPitch = 40;  // halves per staged row: 32 columns + 8 pad (80 B, conflict-free)
+        uint16_t* E = reinterpret_cast<uint16_t*>(&S) + wave * (128 * kPitch);
         const float gwg = P.b_g[(int64_t)expert * P.N + bcol0[0] + colL];
         const float gwu = P.b_g[(int64_t)expert * P.N + bcol0[1] + colL];
-        const int64_t lane_off = (int64_t)rowL * P.ld_out + bcol0[0] + colL;
-        const int32_t part = bcol0[0] >> 5;
 #pragma unroll
         for (int i = 0; i < NSUB; i++) {
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int32_t rowu = row0 + 32 * i + (r >> 2) * 8 + (r & 3);  // uniform
-                const int32_t row = rowu + rowL;
-                const bool valid = row < row_end;  // uniform within each half-wave
-                const float gx = valid ? P.a_g[row] : 0.0f;
-                const float pr = valid ? P.row_prob[row] : 0.0f;
+                // Rows past row_end (an expert's padding) are computed from
+                // in-bounds scale/probability entries and never stored.
+                const int rl = 32 * i + (r >> 2) * 8 + rowL + (r & 3);
+                const int32_t row = row0 + rl;
+                const float gx = P.a_g[row];
+                const float pr = P.row_prob[row];
                 const float yg = bf16_to_f32(bf16_hw(acc[i][0][r] * (gx * gwg)));
                 const float yu = bf16_to_f32(bf16_hw(acc[i][1][r] * (gx * gwu)));
-                const uint32_t hb = bf16_hw(silu_fast(yg) * yu * pr);
-                // max |h| over the wave's 32 columns of this row: the BF16 bit
-                // patterns of |h| order like their values, so integer max is exact.
-                const uint32_t m = half_wave_max_u32(hb & 0x7FFFu);
-                if (valid) {
-                    P.out[(int64_t)rowu * P.ld_out + lane_off] = (uint16_t)hb;
-                    if (colL == 0) P.amax_part[(int64_t)row * P.n_part + part] = __uint_as_float(m << 16);
+                E[rl * kPitch + colL] = (uint16_t)bf16_hw(silu_fast(yg) * yu * pr);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        const int32_t hc = bcol0[0];
+        const int32_t part = hc >> 5;
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+            const int rl = lane + 64 * half;
+            if (rl < 32 * NSUB) {
+                const u32x4* src = reinterpret_cast<const u32x4*>(E + rl * kPitch);
+                u32x4 v[4];
+                u16x2 m = {0, 0};
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    v[q] = src[q];
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v[q][j] & 0x7FFF7FFFu));
+                }
+                const int32_t row = row0 + rl;
+                if (row < row_end) {
+                    u32x4* dst = reinterpret_cast<u32x4*>(P.out + (int64_t)row * P.ld_out + hc);
+#pragma unroll
+                    for (int q = 0; q < 4; q++) dst[q] = v[q];
+                    // max |h| over these 32 columns: BF16 bit patterns of |h|
+                    // order like their values, so the integer max is exact.
+                    const uint32_t mb = max((uint32_t)m[0], (uint32_t)m[1]);
+                    P.amax_part[(int64_t)row * P.n_part + part] = __uint_as_float(mb << 16);
                 }
             }
         }
     } else {
+        constexpr int kPitch = 72;  // halves per staged row: 64 columns + 8 pad (144 B, conflict-free)
+        uint16_t* E = reinterpret_cast<uint16_t*>(&S) + wave * (32 * kPitch);
         const float gw0 = P.b_g[(int64_t)expert * P.N + bcol0[0] + colL];
         const float gw1 = P.b_g[(int64_t)expert * P.N + bcol0[1] + colL];
-        const int64_t lane_off = (int64_t)rowL * P.ld_out + bcol0[0] + colL;
+        // one 32-row MFMA tile per pass
 #pragma unroll
         for (int i = 0; i < NSUB; i++) {
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int32_t rowu = row0 + 32 * i + (r >> 2) * 8 + (r & 3);  // uniform
-                const int32_t row = rowu + rowL;
-                if (row < row_end) {
-                    const float ga = P.a_g[row];
-                    uint16_t* o = P.out + (int64_t)rowu * P.ld_out + lane_off;
-                    o[0] = (uint16_t)bf16_hw(acc[i][0][r] * (ga * gw0));
-                    o[32] = (uint16_t)bf16_hw(acc[i][1][r] * (ga * gw1));
-                }
+                const int rl = (r >> 2) * 8 + rowL + (r & 3);
+                const float ga = P.a_g[row0 + 32 * i + rl];  // in bounds; rows past row_end are not stored
+                E[rl * kPitch + colL] = (uint16_t)bf16_hw(acc[i][0][r] * (ga * gw0));
+                E[rl * kPitch + 32 + colL] = (uint16_t)bf16_hw(acc[i][1][r] * (ga * gw1));
             }
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_wave_barrier();
+            const int32_t row = row0 + 32 * i + lane;
+            if (lane < 32 && row < row_end) {
+                const u32x4* src = reinterpret_cast<const u32x4*>(E + lane * kPitch);
+                u32x4* dst = reinterpret_cast<u32x4*>(P.out + (int64_t)row * P.ld_out + bcol0[0]);
+#pragma unroll
+                for (int q = 0; q < 8; q++) dst[q] = src[q];
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // reads done before the next pass overwrites the slice
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }
