@@ -85,14 +85,31 @@ struct SharedA {
     half8 a[2][4][2][4][64];
 };
 
+// LDS: the next 128-column step's raw weight codes, written by direct
+// global->LDS loads, [wave][chunk][column tile][lane] x 16 bytes.
+struct SharedB {
+    u32x4 b[kWaves][2][2][64];
+};
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt(0), and lgkmcnt(0).
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// Workgroup barrier that orders this wave's LDS reads and writes only: the
+// next steps' global and global->LDS loads stay in flight (their wave-private
+// destinations are waited for separately).  The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int MODE, int NSUB>
-__device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, int32_t row0, int32_t expert,
+__device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, SharedB& SB, int32_t row0, int32_t expert,
                                            int32_t row_end, int32_t nt) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // wave index as a scalar, so per-wave conditions are scalar branches
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t K = P.K;
     const int64_t kc64 = K >> 6, kc128 = K >> 7;
 
-    // This wave's two weight column tiles.
+    // This wave's two weight column tiles (wave 0's always exist).
     int32_t bcol0[2];
     bool active;
     if (MODE == kGemmSwiGLU) {
@@ -106,15 +123,20 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, int3
         bcol0[0] = c;
         bcol0[1] = c + 32;
     }
+    // Every load below is issued unconditionally from an in-bounds address
+    // (an idle wave reads wave 0's columns or row tile 0; the last step
+    // re-reads its own operands), so no loaded value joins a conditional
+    // default and the compiler never has to wait for it early.
+    const int32_t wcol = active ? 0 : (MODE == kGemmSwiGLU ? 32 : 64) * wave;
     int64_t rtb[2];
 #pragma unroll
-    for (int j = 0; j < 2; j++) rtb[j] = ((int64_t)expert * P.N + bcol0[j]) >> 5;
+    for (int j = 0; j < 2; j++) rtb[j] = ((int64_t)expert * P.N + bcol0[j] - wcol) >> 5;
 
     // The activation units this wave decodes for every 128-column step: its
     // 32-row tile `wave`, both 64-column chunks.
     const int ai = wave;
     const bool adec = ai < NSUB;
-    const int64_t rta = (row0 >> 5) + ai;
+    const int64_t rta = (row0 >> 5) + (adec ? ai : 0);
 
     const uint8_t* a_c = P.a_codes + lane * 16;
     const uint8_t* a_s = P.a_scales + lane * 4;
@@ -128,26 +150,25 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, int3
         acc[i][1] = f32x16{};
     }
 
-    u32x4 ua[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-    uint32_t usa = 0u;
-    u32x4 ub[2][2];  // [chunk][column tile]
-    uint32_t usb[2] = {0u, 0u};
-    auto load = [&](int64_t cp, u32x4 (&xa)[2], uint32_t& ya, u32x4 (&xb)[2][2], uint32_t (&yb)[2]) {
-        if (adec) {
+    auto load_a = [&](int64_t cp, u32x4 (&xa)[2], uint32_t& ya) {
 #pragma unroll
-            for (int ch = 0; ch < 2; ch++)
-                xa[ch] = *reinterpret_cast<const u32x4*>(a_c + (rta * kc64 + 2 * cp + ch) * 1024);
-            ya = *reinterpret_cast<const uint32_t*>(a_s + (rta * kc128 + cp) * 256);
-        }
-        if (active) {
+        for (int ch = 0; ch < 2; ch++) xa[ch] = *reinterpret_cast<const u32x4*>(a_c + (rta * kc64 + 2 * cp + ch) * 1024);
+        ya = *reinterpret_cast<const uint32_t*>(a_s + (rta * kc128 + cp) * 256);
+    };
+    auto load_bs = [&](int64_t cp, uint32_t (&yb)[2]) {
 #pragma unroll
-            for (int ch = 0; ch < 2; ch++)
+        for (int j = 0; j < 2; j++) yb[j] = *reinterpret_cast<const uint32_t*>(b_s + (rtb[j] * kc128 + cp) * 256);
+    };
+    // Weight codes of step cp straight into this wave's LDS slice (lane l's
+    // 16 bytes land at slice + 16 l); no registers are held while in flight.
+    auto dma_b = [&](int64_t cp) {
 #pragma unroll
-                for (int j = 0; j < 2; j++)
-                    xb[ch][j] = *reinterpret_cast<const u32x4*>(b_c + (rtb[j] * kc64 + 2 * cp + ch) * 1024);
+        for (int ch = 0; ch < 2; ch++)
 #pragma unroll
-            for (int j = 0; j < 2; j++) yb[j] = *reinterpret_cast<const uint32_t*>(b_s + (rtb[j] * kc128 + cp) * 256);
-        }
+            for (int j = 0; j < 2; j++)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(b_c + (rtb[j] * kc64 + 2 * cp + ch) * 1024),
+                    (__attribute__((address_space(3))) void*)&SB.b[wave][ch][j][0], 16, 0, 0);
     };
     auto decode_a = [&](int buf, const u32x4 (&xa)[2], uint32_t ya) {
         if (!adec) return;
@@ -160,17 +181,29 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, int3
         for (int ks = 0; ks < 4; ks++) S.a[buf][ai][1][ks][lane] = decode8(xa[1][ks], ks < 2 ? lo1 : hi1);
     };
 
-    load(0, ua, usa, ub, usb);
-    decode_a(0, ua, usa);
-    __syncthreads();
+    u32x4 ub[2][2];  // this step's weight codes [chunk][column tile]
+    uint32_t usb[2];
+    {
+        u32x4 ua[2];
+        uint32_t usa;
+        load_a(0, ua, usa);
+#pragma unroll
+        for (int ch = 0; ch < 2; ch++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) ub[ch][j] = *reinterpret_cast<const u32x4*>(b_c + (rtb[j] * kc64 + ch) * 1024);
+        load_bs(0, usb);
+        if (kc128 > 1) dma_b(1);
+        decode_a(0, ua, usa);
+    }
+    barrier_lds();
     for (int64_t cp = 0; cp < kc128; cp++) {
         const int buf = (int)(cp & 1);
-        u32x4 na[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-        uint32_t nsa = 0u;
-        u32x4 nb[2][2];
-        uint32_t nsb[2] = {0u, 0u};
         const bool more = cp + 1 < kc128;
-        if (more) load(cp + 1, na, nsa, nb, nsb);
+        const int64_t cpn = more ? cp + 1 : cp;
+        u32x4 na[2];
+        uint32_t nsa, nsb[2];
+        load_a(cpn, na, nsa);
+        load_bs(cpn, nsb);
         if (active) {
             // Eight k-steps of 16 columns; the A operands of step s+1 are read from
             // LDS while the MFMAs of step s run.
@@ -194,6 +227,9 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, int3
                 half8 bv[2];
 #pragma unroll
                 for (int j = 0; j < 2; j++) bv[j] = decode8(ub[ch][j][ks], bsc[ch][j][ks >> 1]);
+                // Keep the reads above ahead of this step's MFMAs (the
+                // scheduler would otherwise sink each read to its first use).
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < NSUB; i++)
 #pragma unroll
@@ -205,16 +241,22 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, int3
                 }
             }
         }
-        if (more) {
-            decode_a(buf ^ 1, na, nsa);
+        if (more) decode_a(buf ^ 1, na, nsa);
+        // Step cp+1's weight codes: landed in LDS (wait for this wave's
+        // loads), into registers, then the slice is refilled for step cp+2.
+        // On the last step this re-reads the slice; the values go unused.
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
 #pragma unroll
-            for (int ch = 0; ch < 2; ch++)
+        for (int ch = 0; ch < 2; ch++)
 #pragma unroll
-                for (int j = 0; j < 2; j++) ub[ch][j] = nb[ch][j];
-            usb[0] = nsb[0];
-            usb[1] = nsb[1];
+            for (int j = 0; j < 2; j++) ub[ch][j] = SB.b[wave][ch][j][lane];
+        usb[0] = nsb[0];
+        usb[1] = nsb[1];
+        if (cp + 2 < kc128) {
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // slice read before it is overwritten
+            dma_b(cp + 2);
         }
-        __syncthreads();
+        barrier_lds();
     }
     if (!active) return;
 
@@ -310,6 +352,7 @@ template <int MODE>
 __global__ void __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_kernel(GemmParams P) {
     __shared__ SharedA S;
+    __shared__ SharedB SB;
     const int64_t n_mt = P.dense_m >= 0 ? (P.dense_m + kTileRows - 1) / kTileRows : *P.n_mtiles;
     const int64_t total = n_mt * P.n_tiles_n;
     const int64_t nb = gridDim.x;  // a multiple of 8
@@ -332,10 +375,10 @@ gemm_kernel(GemmParams P) {
             row_end = d.w;
         }
         switch (nsub) {
-            case 4: block_tile<MODE, 4>(P, S, row0, expert, row_end, nt); break;
-            case 3: block_tile<MODE, 3>(P, S, row0, expert, row_end, nt); break;
-            case 2: block_tile<MODE, 2>(P, S, row0, expert, row_end, nt); break;
-            default: block_tile<MODE, 1>(P, S, row0, expert, row_end, nt); break;
+            case 4: block_tile<MODE, 4>(P, S, SB, row0, expert, row_end, nt); break;
+            case 3: block_tile<MODE, 3>(P, S, SB, row0, expert, row_end, nt); break;
+            case 2: block_tile<MODE, 2>(P, S, SB, row0, expert, row_end, nt); break;
+            default: block_tile<MODE, 1>(P, S, SB, row0, expert, row_end, nt); break;
         }
         __syncthreads();  // the next tile's prologue overwrites LDS buffer 0
     }
