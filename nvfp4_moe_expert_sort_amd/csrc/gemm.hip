@@ -143,6 +143,16 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
     const uint8_t* b_c = P.b_codes + lane * 16;
     const uint8_t* b_s = P.b_scales + lane * 4;
 
+    // Plain mode: row scales of the tile's rows for the epilogue, fetched before
+    // the K loop; lane l holds rows l and 64 + l (clamped to the tile's rows).
+    const int colL = lane & 31;
+    constexpr int kLastRow = 32 * NSUB - 1;
+    float rg0 = 0.0f, rg1 = 0.0f;
+    if (MODE == kGemmPlain) {
+        rg0 = P.a_g[row0 + min(lane, kLastRow)];
+        rg1 = NSUB > 2 ? P.a_g[row0 + min(64 + lane, kLastRow)] : 0.0f;
+    }
+
     f32x16 acc[NSUB][2];
 #pragma unroll
     for (int i = 0; i < NSUB; i++) {
@@ -264,15 +274,24 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
     // (r/4)*8 + (l/32)*4 + r%4 and column l%32 of that 32x32 tile.  Results go
     // through this wave's own slice of the (now idle) LDS operand buffers, so
     // global stores are 16 bytes per lane and each row's max |h| is a
-    // lane-local reduction.  The slice is wave-private; the barrier at the end
-    // of the tile loop orders it against the next tile's LDS writes.
-    const int colL = lane & 31;
+    // lane-local reduction.  In plain mode the tile's row scales go to the
+    // wave's raw-weight slice, from where the four consecutive rows of a
+    // register group are one broadcast read.  Both slices are wave-private and
+    // LDS accesses of one wave complete in order; the barrier at the end of
+    // the tile loop orders them against the next tile's LDS writes.  Nothing
+    // here waits for the global stores.
     const int rowL = (lane >> 5) * 4;
+    float cg[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) cg[j] = P.b_g[(int64_t)expert * P.N + bcol0[j] + colL];
+    float* RS = reinterpret_cast<float*>(&SB.b[wave][0][0][0]);
+    if (MODE == kGemmPlain) {
+        RS[lane] = rg0;
+        RS[64 + lane] = rg1;
+    }
     if (MODE == kGemmSwiGLU) {
         constexpr int kPitch = 40;  // halves per staged row: 32 columns + 8 pad (80 B, conflict-free)
         uint16_t* E = reinterpret_cast<uint16_t*>(&S) + wave * (128 * kPitch);
-        const float gwg = P.b_g[(int64_t)expert * P.N + bcol0[0] + colL];
-        const float gwu = P.b_g[(int64_t)expert * P.N + bcol0[1] + colL];
 #pragma unroll
         for (int i = 0; i < NSUB; i++) {
 #pragma unroll
@@ -283,12 +302,12 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
                 const int32_t row = row0 + rl;
                 const float gx = P.a_g[row];
                 const float pr = P.row_prob[row];
-                const float yg = bf16_to_f32(bf16_hw(acc[i][0][r] * (gx * gwg)));
-                const float yu = bf16_to_f32(bf16_hw(acc[i][1][r] * (gx * gwu)));
+                const float yg = bf16_to_f32(bf16_hw(acc[i][0][r] * (gx * cg[0])));
+                const float yu = bf16_to_f32(bf16_hw(acc[i][1][r] * (gx * cg[1])));
                 E[rl * kPitch + colL] = (uint16_t)bf16_hw(silu_fast(yg) * yu * pr);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_wave_barrier();
         const int32_t hc = bcol0[0];
         const int32_t part = hc >> 5;
@@ -321,28 +340,32 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
     } else {
         constexpr int kPitch = 72;  // halves per staged row: 64 columns + 8 pad (144 B, conflict-free)
         uint16_t* E = reinterpret_cast<uint16_t*>(&S) + wave * (32 * kPitch);
-        const float gw0 = P.b_g[(int64_t)expert * P.N + bcol0[0] + colL];
-        const float gw1 = P.b_g[(int64_t)expert * P.N + bcol0[1] + colL];
-        // one 32-row MFMA tile per pass
+        // one 32-row MFMA tile per pass; lane l then stores half (l/32) of row l%32
 #pragma unroll
         for (int i = 0; i < NSUB; i++) {
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int rl = (r >> 2) * 8 + rowL + (r & 3);
-                const float ga = P.a_g[row0 + 32 * i + rl];  // in bounds; rows past row_end are not stored
-                E[rl * kPitch + colL] = (uint16_t)bf16_hw(acc[i][0][r] * (ga * gw0));
-                E[rl * kPitch + 32 + colL] = (uint16_t)bf16_hw(acc[i][1][r] * (ga * gw1));
-            }
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_wave_barrier();
-            const int32_t row = row0 + 32 * i + lane;
-            if (lane < 32 && row < row_end) {
-                const u32x4* src = reinterpret_cast<const u32x4*>(E + lane * kPitch);
-                u32x4* dst = reinterpret_cast<u32x4*>(P.out + (int64_t)row * P.ld_out + bcol0[0]);
+            for (int q = 0; q < 4; q++) {
+                const int rb = 8 * q + rowL;  // first of this lane's four rows in the pass
+                const float4 g4 = *reinterpret_cast<const float4*>(RS + 32 * i + rb);  // rows past row_end are not stored
+                const float ga[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
-                for (int q = 0; q < 8; q++) dst[q] = src[q];
+                for (int e = 0; e < 4; e++) {
+                    const int r = 4 * q + e;
+                    E[(rb + e) * kPitch + colL] = (uint16_t)bf16_hw(acc[i][0][r] * (ga[e] * cg[0]));
+                    E[(rb + e) * kPitch + 32 + colL] = (uint16_t)bf16_hw(acc[i][1][r] * (ga[e] * cg[1]));
+                }
             }
-            __builtin_amdgcn_s_waitcnt(0);  // reads done before the next pass overwrites the slice
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            __builtin_amdgcn_wave_barrier();
+            const int32_t row = row0 + 32 * i + colL;
+            const int hseg = lane >> 5;
+            if (row < row_end) {
+                const u32x4* src = reinterpret_cast<const u32x4*>(E + colL * kPitch + 32 * hseg);
+                u32x4* dst = reinterpret_cast<u32x4*>(P.out + (int64_t)row * P.ld_out + bcol0[0] + 32 * hseg);
+#pragma unroll
+                for (int q = 0; q < 4; q++) dst[q] = src[q];
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // slice read before the next pass overwrites it
             __builtin_amdgcn_wave_barrier();
         }
     }
@@ -380,7 +403,7 @@ gemm_kernel(GemmParams P) {
             case 2: block_tile<MODE, 2>(P, S, SB, row0, expert, row_end, nt); break;
             default: block_tile<MODE, 1>(P, S, SB, row0, expert, row_end, nt); break;
         }
-        __syncthreads();  // the next tile's prologue overwrites LDS buffer 0
+        barrier_lds();  // the next tile's prologue overwrites LDS buffer 0
     }
 }
 
