@@ -42,9 +42,20 @@ __global__ void __launch_bounds__(256) quant_h_kernel(const uint16_t* __restrict
     const int hh = lane >> 5, rl = lane & 31;
     const int64_t row = rt * 32 + rl;
     const bool valid = row2pair[row] >= 0;  // padding rows are written as zeros
+    // The h loads go out first (padding rows read in-bounds values that are
+    // never used), then the row's partial maxima: n_part = I / 32 floats,
+    // 16-byte aligned since I % 128 == 0.
+    u32x4 v[2][4];
+#pragma unroll
+    for (int ch = 0; ch < 2; ch++) load32(h + row * I + 64 * (2 * cp + ch) + 32 * hh, false, v[ch]);
+    const float4* part = reinterpret_cast<const float4*>(amax2_part + row * n_part);
     float amax = 0.0f;
-    if (valid)
-        for (int i = 0; i < n_part; i++) amax = fmaxf(amax, amax2_part[row * n_part + i]);
+#pragma unroll 8
+    for (int i = 0; i < n_part / 4; i++) {
+        const float4 q = part[i];
+        amax = fmaxf(amax, fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w)));
+    }
+    if (!valid) amax = 0.0f;
     const RowScale rs = row_scale(amax);
     uint32_t sc = 0u;
 #pragma unroll
@@ -52,11 +63,7 @@ __global__ void __launch_bounds__(256) quant_h_kernel(const uint16_t* __restrict
         const int64_t c = 2 * cp + ch;
         u32x4 cw = {0u, 0u, 0u, 0u};
         uint32_t s2 = 0u;
-        if (valid) {
-            u32x4 v[4];
-            load32(h + row * I + 64 * c + 32 * hh, false, v);
-            quant32(v, rs, round_up != 0, false, cw, s2);
-        }
+        if (valid) quant32(v[ch], rs, round_up != 0, false, cw, s2);
         *reinterpret_cast<u32x4*>(codes + (rt * (I / 64) + c) * 1024 + lane * 16) = cw;
         sc |= s2 << (16 * ch);
     }
