@@ -6,17 +6,18 @@
 //
 // Four launches, all sized from T and the config only (no host read-back of
 // counts, article section 4.6):
-//   route_count   per block of 16 tokens: one pass over each token row takes
-//                 its amax and quantizes it once (token-major buffer Xq);
-//                 the block's (t, k) pairs get stable per-expert ranks in pair
-//                 order (wave ballots) and a per-expert block count; id checks.
+//   route_count   per block of 16 tokens, one wavefront per token: the row
+//                 is read once into registers for its amax and quantization
+//                 (token-major buffer Xq); the block's (t, k) pairs get stable
+//                 per-expert ranks in pair order (wave ballots) and a
+//                 per-expert block count; id checks.
 //   route_scan    one block: per-expert exclusive prefix over the blocks,
 //                 padded expert offsets off[E+1], the GEMM row-tile table,
 //                 padding rows marked, error word.
 //   route_place   per pair: sorted row = off[e] + block prefix + rank.
-//   route_gather  per (32-row tile, 128 columns): builds the padded, sorted
-//                 GEMM-layout buffer from Xq, writing whole 1 KiB chunks;
-//                 padding rows are written as zeros.
+//   route_gather  per (32-row tile, up to 256 columns): builds the padded,
+//                 sorted GEMM-layout buffer from Xq, writing whole 1 KiB
+//                 chunks; padding rows are written as zeros.
 // Integer atomics only on LDS counters: every count and row index is
 // independent of scheduling.
 #include <algorithm>
@@ -27,16 +28,56 @@
 
 namespace nvfp4 {
 
-__global__ void __launch_bounds__(256) route_count_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
-                                                          int32_t T, int32_t H, int32_t K, int32_t E, int round_up,
-                                                          int32_t* __restrict__ blk_counts,
-                                                          int32_t* __restrict__ blk_err, int32_t* __restrict__ lrank,
-                                                          uint8_t* __restrict__ xq_codes,
-                                                          uint8_t* __restrict__ xq_scales, float* __restrict__ gx) {
+// One token row per wavefront, held in registers: lane l owns the 32-element
+// groups l, l + 64, ... (G of them), so the row is read once for its amax and
+// its quantization.  Same arithmetic as quant_row_wave (logical layout).
+template <int G>
+__device__ __forceinline__ void quant_row_regs(const uint16_t* __restrict__ x, int64_t cols, bool round_up, int64_t r,
+                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                               float* __restrict__ gout) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t groups = cols >> 5;  // cols % 32 == 0
+    u32x4 v[G][4];
+    uint32_t m = 0u;
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        const int64_t gi = lane + kWave * g;
+        if (gi < groups) {
+            load32(x + gi * 32, false, v[g]);
+            m = max(m, max(max(absmax8_bits(v[g][0]), absmax8_bits(v[g][1])),
+                           max(absmax8_bits(v[g][2]), absmax8_bits(v[g][3]))));
+        }
+    }
+    const RowScale rs = row_scale(bf16_to_f32(wave_max_u32(m)));
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        const int64_t gi = lane + kWave * g;
+        if (gi < groups) {
+            u32x4 c;
+            uint32_t s2;
+            quant32(v[g], rs, round_up, false, c, s2);
+            *reinterpret_cast<u32x4*>(codes + r * (cols >> 1) + gi * 16) = c;
+            *reinterpret_cast<uint16_t*>(scales + r * (cols >> 4) + gi * 2) = (uint16_t)s2;
+        }
+    }
+    if (lane == 0) gout[r] = rs.g;
+}
+
+constexpr int kCountThreads = kTokPerBlk * 64;  // one wavefront per token of the block
+
+__global__ void __launch_bounds__(kCountThreads) route_count_kernel(const uint16_t* __restrict__ x,
+                                                                    const int32_t* __restrict__ ids, int32_t T,
+                                                                    int32_t H, int32_t K, int32_t E, int round_up,
+                                                                    int32_t* __restrict__ blk_counts,
+                                                                    int32_t* __restrict__ blk_err,
+                                                                    int32_t* __restrict__ lrank,
+                                                                    uint8_t* __restrict__ xq_codes,
+                                                                    uint8_t* __restrict__ xq_scales,
+                                                                    float* __restrict__ gx) {
     __shared__ int32_t cnt[kMaxExperts];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t t0 = (int64_t)blockIdx.x * kTokPerBlk;
-    for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
+    for (int e = tid; e < E; e += kCountThreads) cnt[e] = 0;
     __syncthreads();
     if (wave == 0) {
         // Stable ranks in pair order: pairs are taken 64 at a time; lanes with
@@ -50,10 +91,16 @@ __global__ void __launch_bounds__(256) route_count_kernel(const uint16_t* __rest
             const int32_t e = p < p1 ? ids[p] : -1;
             const bool valid = e >= 0 && e < E;
             if (p < p1 && !valid) err |= 1;
-            if (valid) {
-                const int64_t t = p / K;
-                for (int64_t q = t * K; q < p; q++)
-                    if (ids[q] == e) err |= 2;
+            // A token may not name an expert twice: compare with the token's
+            // earlier slots, taken from the lanes that hold them (or memory
+            // when the token began in the previous group of 64).
+            const int kk = (int)(p % K);
+            for (int d = 1; d < K; d++) {
+                const int32_t ed = __shfl(e, max(lane - d, 0), kWave);
+                if (valid && d <= kk) {
+                    const int32_t prev = lane >= d ? ed : ids[p - d];
+                    if (prev == e) err |= 2;
+                }
             }
             uint64_t mask = __ballot(valid);
             for (int b = 0; b < nbits; b++) {
@@ -73,28 +120,60 @@ __global__ void __launch_bounds__(256) route_count_kernel(const uint16_t* __rest
         for (int o = 32; o > 0; o >>= 1) err |= __shfl_xor(err, o, kWave);
         if (lane == 0) blk_err[blockIdx.x] = err;
     }
-    // Each wave quantizes whole token rows once (amax in the same pass).
-    for (int64_t t = t0 + wave; t < min(t0 + kTokPerBlk, (int64_t)T); t += 4)
-        quant_row_wave(x + t * H, H, -1.0f, round_up != 0, false, t, xq_codes, xq_scales, gx);
+    // Each wave quantizes its token's row once (amax in the same pass).
+    const int64_t t = t0 + wave;
+    if (t < T) {
+        const int64_t groups_per_lane = (H / 32 + kWave - 1) / kWave;
+        const uint16_t* xr = x + t * H;
+        const bool ru = round_up != 0;
+        switch (groups_per_lane) {
+            case 1: quant_row_regs<1>(xr, H, ru, t, xq_codes, xq_scales, gx); break;
+            case 2: quant_row_regs<2>(xr, H, ru, t, xq_codes, xq_scales, gx); break;
+            case 3: quant_row_regs<3>(xr, H, ru, t, xq_codes, xq_scales, gx); break;
+            case 4: quant_row_regs<4>(xr, H, ru, t, xq_codes, xq_scales, gx); break;
+            default: quant_row_wave(xr, H, -1.0f, ru, false, t, xq_codes, xq_scales, gx); break;
+        }
+    }
     __syncthreads();
-    for (int e = tid; e < E; e += blockDim.x) blk_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
+    for (int e = tid; e < E; e += kCountThreads) blk_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// Block-wide inclusive scan of one int per thread (1024 threads).
-__device__ int32_t block_scan_incl(int32_t v, int32_t* buf) {
-    const int tid = threadIdx.x;
-    buf[tid] = v;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-        int32_t add = tid >= o ? buf[tid - o] : 0;
-        __syncthreads();
-        buf[tid] += add;
-        __syncthreads();
+// Block-wide inclusive scan of two ints per thread (1024 threads = 16 waves):
+// shuffles within each wave, then one wave scans the 16 wave totals.
+__device__ int2 block_scan_incl2(int2 v, int2* wsum /* [16] */) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int nx = __shfl_up(v.x, o, kWave), ny = __shfl_up(v.y, o, kWave);
+        if (lane >= o) {
+            v.x += nx;
+            v.y += ny;
+        }
     }
-    int32_t r = buf[tid];
+    if (lane == 63) wsum[wave] = v;
     __syncthreads();
-    return r;
+    if (wave == 0) {
+        int2 w = lane < 16 ? wsum[lane] : make_int2(0, 0);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int nx = __shfl_up(w.x, o, kWave), ny = __shfl_up(w.y, o, kWave);
+            if (lane >= o) {
+                w.x += nx;
+                w.y += ny;
+            }
+        }
+        if (lane < 16) wsum[lane] = w;
+    }
+    __syncthreads();
+    if (wave > 0) {
+        const int2 b = wsum[wave - 1];
+        v.x += b.x;
+        v.y += b.y;
+    }
+    return v;
 }
+
+constexpr int kScanRegs = 32;  // block counts a scan thread keeps in registers
 
 __global__ void __launch_bounds__(1024) route_scan_kernel(int32_t nblk, int32_t E, int32_t* __restrict__ blk_counts,
                                                           const int32_t* __restrict__ blk_err,
@@ -103,28 +182,28 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(int32_t nblk, int32_t 
                                                           int4* __restrict__ mtiles, int32_t* __restrict__ n_mtiles,
                                                           int32_t* __restrict__ row2pair, int32_t* __restrict__ err_word) {
     __shared__ int32_t part[1024];
-    __shared__ int32_t scan_buf[1024];
+    __shared__ int2 wsum[16];
     __shared__ int32_t errs;
     const int tid = threadIdx.x;
     if (tid == 0) errs = 0;
     // (1) per-expert exclusive prefix over blocks: tpe threads per expert, each
-    //     owning a contiguous segment of blocks; loads issued 8 at a time.
+    //     owning a contiguous segment of blocks.  Segments of up to kScanRegs
+    //     blocks are read once into registers with all loads in flight.
     const int tpe = 1024 / E;  // >= 1 since E <= 1024
     const int e1 = tid % E, sub = tid / E;  // consecutive lanes read consecutive experts (coalesced)
     // (threads with sub >= tpe own no segment)
     const int seg = (nblk + tpe - 1) / tpe;
     const int b0 = min(sub * seg, nblk), b1 = sub < tpe ? min(b0 + seg, nblk) : b0;
+    const bool in_regs = seg <= kScanRegs;
+    int32_t v[kScanRegs];
     int32_t sum = 0;
-    if (sub < tpe) {
-        int b = b0;
-        for (; b + 8 <= b1; b += 8) {
-            int32_t v[8];
+    if (in_regs) {
 #pragma unroll
-            for (int j = 0; j < 8; j++) v[j] = blk_counts[(int64_t)(b + j) * E + e1];
+        for (int j = 0; j < kScanRegs; j++) v[j] = b0 + j < b1 ? blk_counts[(int64_t)(b0 + j) * E + e1] : 0;
 #pragma unroll
-            for (int j = 0; j < 8; j++) sum += v[j];
-        }
-        for (; b < b1; b++) sum += blk_counts[(int64_t)b * E + e1];
+        for (int j = 0; j < kScanRegs; j++) sum += v[j];
+    } else {
+        for (int b = b0; b < b1; b++) sum += blk_counts[(int64_t)b * E + e1];
     }
     if (sub < tpe) part[e1 * tpe + sub] = sum;
     int my_err = 0;
@@ -134,24 +213,20 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(int32_t nblk, int32_t 
     if (sub < tpe) {
         int32_t run = 0;
         for (int s = 0; s < sub; s++) run += part[e1 * tpe + s];
-        int b = b0;
-        for (; b + 8 <= b1; b += 8) {
-            int32_t v[8];
+        if (in_regs) {
 #pragma unroll
-            for (int j = 0; j < 8; j++) v[j] = blk_counts[(int64_t)(b + j) * E + e1];
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                blk_counts[(int64_t)(b + j) * E + e1] = run;  // this block's first rank within expert e1
+            for (int j = 0; j < kScanRegs; j++) {
+                if (b0 + j < b1) blk_counts[(int64_t)(b0 + j) * E + e1] = run;  // the block's first rank within e1
                 run += v[j];
             }
-        }
-        for (; b < b1; b++) {
-            const int32_t c = blk_counts[(int64_t)b * E + e1];
-            blk_counts[(int64_t)b * E + e1] = run;
-            run += c;
+        } else {
+            for (int b = b0; b < b1; b++) {
+                const int32_t c = blk_counts[(int64_t)b * E + e1];
+                blk_counts[(int64_t)b * E + e1] = run;
+                run += c;
+            }
         }
     }
-    __syncthreads();
     // (2) totals, padded offsets and row-tile counts per expert (thread e).
     int32_t cnt = 0, padded = 0, ntile = 0;
     if (tid < E) {
@@ -159,16 +234,15 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(int32_t nblk, int32_t 
         padded = (cnt + kMAlign - 1) / kMAlign * kMAlign;
         ntile = (padded + kTileRows - 1) / kTileRows;
     }
-    const int32_t off_incl = block_scan_incl(padded, scan_buf);
-    const int32_t tile_incl = block_scan_incl(ntile, scan_buf);
+    const int2 incl = block_scan_incl2(make_int2(padded, ntile), wsum);
     if (tid < E) {
-        const int32_t off = off_incl - padded;
-        const int32_t t0 = tile_incl - ntile;
+        const int32_t off = incl.x - padded;
+        const int32_t t0 = incl.y - ntile;
         expert_count[tid] = cnt;
         expert_off[tid] = off;
         if (tid == E - 1) {
-            expert_off[E] = off_incl;
-            *n_mtiles = tile_incl;
+            expert_off[E] = incl.x;
+            *n_mtiles = incl.y;
             *err_word = errs;
         }
         for (int i = 0; i < ntile; i++) {
@@ -202,9 +276,12 @@ __global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restr
     row_prob[row] = probs[p];
 }
 
-// One wave per (32-row tile, 128-column step) of the sorted buffer: lane
-// (h*32 + r) copies row r's columns [64c + 32h, +32) for c = 2*cp, 2*cp+1 from
-// its token's quantized row, so each chunk is written as one contiguous 1 KiB.
+constexpr int kGatherSteps = 2;  // 128-column steps per gather wave
+
+// One wave per (32-row tile, up to kGatherSteps 128-column steps) of the
+// sorted buffer: lane (h*32 + r) copies row r's columns [64c + 32h, +32) of
+// each chunk c from its token's quantized row, so every chunk is written as
+// one contiguous 1 KiB; all loads are issued before the stores.
 __global__ void __launch_bounds__(256) route_gather_kernel(int32_t H, int32_t K, const int32_t* __restrict__ expert_off,
                                                            int32_t E, const int32_t* __restrict__ row2pair,
                                                            const uint8_t* __restrict__ xq_codes,
@@ -215,35 +292,45 @@ __global__ void __launch_bounds__(256) route_gather_kernel(int32_t H, int32_t K,
     const int lane = threadIdx.x & 63;
     const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (unit >= n_units) return;
-    const int64_t cps = H / 128;
-    const int64_t rt = unit / cps, cp = unit % cps;
+    const int64_t cps = H / 128, groups = (cps + kGatherSteps - 1) / kGatherSteps;
+    const int64_t rt = unit / groups, cp0 = (unit % groups) * kGatherSteps;
     if (rt * 32 >= expert_off[E]) return;  // past the last expert's rows
     const int h = lane >> 5, rl = lane & 31;
     const int64_t row = rt * 32 + rl;
     const int32_t p = row2pair[row];
-    u32x4 c0 = {0u, 0u, 0u, 0u}, c1 = {0u, 0u, 0u, 0u};
-    uint32_t s0 = 0u, s1 = 0u;
-    float g = 0.0f;
-    if (p >= 0) {
-        const int64_t t = p / K;
-        const uint8_t* cs = xq_codes + t * (H / 2) + (2 * cp) * 32 + h * 16;
-        const uint8_t* ss = xq_scales + t * (H / 16) + (2 * cp) * 4 + h * 2;
-        c0 = *reinterpret_cast<const u32x4*>(cs);
-        c1 = *reinterpret_cast<const u32x4*>(cs + 32);
-        s0 = *reinterpret_cast<const uint16_t*>(ss);
-        s1 = *reinterpret_cast<const uint16_t*>(ss + 4);
-        g = gx[t];
+    const int64_t t = p >= 0 ? p / K : 0;
+    const uint8_t* cs = xq_codes + t * (H / 2) + h * 16;
+    const uint8_t* ss = xq_scales + t * (H / 16) + h * 2;
+    u32x4 c[kGatherSteps][2];
+    uint32_t sc[kGatherSteps];
+#pragma unroll
+    for (int i = 0; i < kGatherSteps; i++) {
+        const int64_t cp = cp0 + i;
+        c[i][0] = c[i][1] = u32x4{0u, 0u, 0u, 0u};
+        sc[i] = 0u;
+        if (p >= 0 && cp < cps) {
+            c[i][0] = *reinterpret_cast<const u32x4*>(cs + cp * 64);
+            c[i][1] = *reinterpret_cast<const u32x4*>(cs + cp * 64 + 32);
+            sc[i] = (uint32_t)*reinterpret_cast<const uint16_t*>(ss + cp * 8) |
+                    ((uint32_t)*reinterpret_cast<const uint16_t*>(ss + cp * 8 + 4) << 16);
+        }
     }
-    *reinterpret_cast<u32x4*>(a_codes + (rt * (H / 64) + 2 * cp) * 1024 + lane * 16) = c0;
-    *reinterpret_cast<u32x4*>(a_codes + (rt * (H / 64) + 2 * cp + 1) * 1024 + lane * 16) = c1;
-    *reinterpret_cast<uint32_t*>(a_scales + (rt * (H / 128) + cp) * 256 + lane * 4) = s0 | (s1 << 16);
-    if (cp == 0 && h == 0) a_g[row] = g;
+#pragma unroll
+    for (int i = 0; i < kGatherSteps; i++) {
+        const int64_t cp = cp0 + i;
+        if (cp < cps) {
+            *reinterpret_cast<u32x4*>(a_codes + (rt * (H / 64) + 2 * cp) * 1024 + lane * 16) = c[i][0];
+            *reinterpret_cast<u32x4*>(a_codes + (rt * (H / 64) + 2 * cp + 1) * 1024 + lane * 16) = c[i][1];
+            *reinterpret_cast<uint32_t*>(a_scales + (rt * (H / 128) + cp) * 256 + lane * 4) = sc[i];
+        }
+    }
+    if (cp0 == 0 && h == 0) a_g[row] = p >= 0 ? gx[t] : 0.0f;
 }
 
 hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* probs, int32_t T, int32_t H, int32_t K,
                         int32_t E, bool round_up, const RouteBuffers& rb, int64_t rows_cap, hipStream_t stream) {
     const int32_t nblk = (T + kTokPerBlk - 1) / kTokPerBlk;
-    hipLaunchKernelGGL(route_count_kernel, dim3(nblk), dim3(256), 0, stream, x, ids, T, H, K, E, round_up ? 1 : 0,
+    hipLaunchKernelGGL(route_count_kernel, dim3(nblk), dim3(kCountThreads), 0, stream, x, ids, T, H, K, E, round_up ? 1 : 0,
                        rb.blk_counts, rb.blk_err, rb.pair2row /* holds the ranks until route_place */, rb.xq_codes,
                        rb.xq_scales, rb.gx);
     hipError_t st = hipGetLastError();
@@ -259,7 +346,7 @@ hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* prob
     if (st != hipSuccess) return st;
     // Row tiles that can hold rows for this T (the device offsets decide which are used).
     const int64_t rows_bound = std::min<int64_t>(rows_cap, (P + (int64_t)E * (kMAlign - 1) + 31) / 32 * 32);
-    const int64_t n_units = rows_bound / 32 * (H / 128);
+    const int64_t n_units = rows_bound / 32 * ((H / 128 + kGatherSteps - 1) / kGatherSteps);
     hipLaunchKernelGGL(route_gather_kernel, dim3((unsigned)((n_units + 3) / 4)), dim3(256), 0, stream, H, K,
                        rb.expert_off, E, rb.row2pair, rb.xq_codes, rb.xq_scales, rb.gx, n_units, rb.a_codes,
                        rb.a_scales, rb.a_g);
