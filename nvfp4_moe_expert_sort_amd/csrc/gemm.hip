@@ -381,27 +381,28 @@ gemm_kernel(GemmParams P) {
     const int64_t nb = gridDim.x;  // a multiple of 8
     const int64_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = nb >> 3;
     const int64_t t_begin = total * xcd / 8, t_end = total * (xcd + 1) / 8;
-    for (int64_t t = t_begin + slot; t < t_end; t += per) {
+    // Each tile's descriptor is loaded one tile ahead, so a tile's first
+    // operand loads do not wait for it.
+    auto tile_desc = [&](int64_t t) -> int4 {
         const int64_t mt = t / P.n_tiles_n;
-        const int32_t nt = (int32_t)(t % P.n_tiles_n);
-        int32_t row0, expert, nsub, row_end;
         if (P.dense_m >= 0) {
-            row0 = (int32_t)(mt * kTileRows);
-            expert = 0;
-            nsub = min(4, (P.dense_m - row0 + kMAlign - 1) / kMAlign);
-            row_end = P.dense_m;
-        } else {
-            const int4 d = P.mtiles[mt];
-            row0 = d.x;
-            expert = d.y;
-            nsub = d.z;
-            row_end = d.w;
+            const int32_t row0 = (int32_t)(mt * kTileRows);
+            return make_int4(row0, 0, min(4, (P.dense_m - row0 + kMAlign - 1) / kMAlign), P.dense_m);
         }
-        switch (nsub) {
-            case 4: block_tile<MODE, 4>(P, S, SB, row0, expert, row_end, nt); break;
-            case 3: block_tile<MODE, 3>(P, S, SB, row0, expert, row_end, nt); break;
-            case 2: block_tile<MODE, 2>(P, S, SB, row0, expert, row_end, nt); break;
-            default: block_tile<MODE, 1>(P, S, SB, row0, expert, row_end, nt); break;
+        return P.mtiles[mt];
+    };
+    int64_t t = t_begin + slot;
+    if (t >= t_end) return;
+    int4 d = tile_desc(t);
+    for (; t < t_end; t += per) {
+        const int32_t nt = (int32_t)(t % P.n_tiles_n);
+        const int4 cur = d;
+        if (t + per < t_end) d = tile_desc(t + per);
+        switch (cur.z) {
+            case 4: block_tile<MODE, 4>(P, S, SB, cur.x, cur.y, cur.w, nt); break;
+            case 3: block_tile<MODE, 3>(P, S, SB, cur.x, cur.y, cur.w, nt); break;
+            case 2: block_tile<MODE, 2>(P, S, SB, cur.x, cur.y, cur.w, nt); break;
+            default: block_tile<MODE, 1>(P, S, SB, cur.x, cur.y, cur.w, nt); break;
         }
         barrier_lds();  // the next tile's prologue overwrites LDS buffer 0
     }
