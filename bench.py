@@ -117,8 +117,9 @@ def main():
     T, H, E, K, I = s.T, s.H, s.E, s.K, s.I
     w1, w2 = wl.weights(threads=16)
     cfg = m.make_config(H, I, E, K, T)
-    qw = m.QuantWeights(cfg, dev).quantize_from(torch.from_numpy(w1.view(np.int16)).to(dev),
-                                                torch.from_numpy(w2.view(np.int16)).to(dev))
+    w1_dev = torch.from_numpy(w1.view(np.int16)).to(dev)
+    w2_dev = torch.from_numpy(w2.view(np.int16)).to(dev)
+    qw = m.QuantWeights(cfg, dev).quantize_from(w1_dev, w2_dev)
     ws = m.alloc_workspace(cfg, dev)
     x = torch.from_numpy(wl.x.view(np.int16)).to(dev)
     ids = torch.from_numpy(wl.ids).to(dev)
@@ -153,6 +154,20 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     stage_ms = np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(m.N_STAGE_EVENTS - 1)] for ev in events])
     stage_mean = stage_ms.mean(axis=0)
+
+    # Weight quantization (once per weight update, outside the forward): W1 and W2
+    # re-quantized in place, timed with events on the stream.
+    wq = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    n_wq = 5
+    wq[0].record(stream)
+    for _ in range(n_wq):
+        qw.quantize_from(w1_dev, w2_dev, stream=stream)
+    wq[1].record(stream)
+    torch.cuda.synchronize()
+    wq_ms = wq[0].elapsed_time(wq[1]) / n_wq
+    wq_rows = E * (2 * I + H)
+    wq_bytes = 2 * E * (2 * I * H + H * I) + E * (2 * I * (H // 2 + H // 16) + H * (I // 2 + I // 16)) + 4 * wq_rows
+    del w1_dev, w2_dev
 
     # Cold-cache forwards (secondary): a 512 MiB write evicts L2 and the 256 MB MALL before each one.
     cold = []
@@ -208,6 +223,9 @@ def main():
                   "fc2_tflops": fc2_flop / (stage_mean[3] / 1e3) / 1e12,
                   "cold_ms_median": float(np.median(cold)) if cold else None,
                   "cold_tokens_per_s": T / (np.median(cold) / 1e3) if cold else None},
+        "weight_quantization": {"ms": wq_ms, "bytes": wq_bytes, "GB_s": wq_bytes / (wq_ms / 1e3) / 1e9,
+                                "frac_hbm_peak": wq_bytes / (wq_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                "what": "W1 [E,2I,H] and W2 [E,H,I] BF16 read, NVFP4 codes/scales/g written"},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, w1, w2, args.cpu_seconds)

@@ -182,4 +182,46 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ x, i
     if (lane == 0) gout[r] = rs.g;
 }
 
+// One row per wavefront, held in registers: lane l owns the 32-element groups
+// l, l + 64, ... (G of them, cols <= 2048 G, cols % 32 == 0), so the row is
+// read once for its amax and its quantization.  Same arithmetic and outputs
+// as quant_row_wave.
+template <int G>
+__device__ __forceinline__ void quant_row_regs(const uint16_t* __restrict__ x, int64_t cols, bool round_up, bool gemm,
+                                               int64_t r, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                               float* __restrict__ gout) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t groups = cols >> 5;
+    u32x4 v[G][4];
+    uint32_t m = 0u;
+#pragma unroll
+    for (int gg = 0; gg < G; gg++) {
+        const int64_t gi = lane + kWave * gg;
+        if (gi < groups) {
+            load32(x + gi * 32, false, v[gg]);
+            m = max(m, max(max(absmax8_bits(v[gg][0]), absmax8_bits(v[gg][1])),
+                           max(absmax8_bits(v[gg][2]), absmax8_bits(v[gg][3]))));
+        }
+    }
+    const RowScale rs = row_scale(bf16_to_f32(wave_max_u32(m)));
+#pragma unroll
+    for (int gg = 0; gg < G; gg++) {
+        const int64_t gi = lane + kWave * gg;
+        if (gi < groups) {
+            u32x4 c;
+            uint32_t s2;
+            quant32(v[gg], rs, round_up, false, c, s2);
+            const int64_t k = gi * 32;
+            if (gemm) {
+                *reinterpret_cast<u32x4*>(codes + gemm_code_off(r, k, cols)) = c;
+                *reinterpret_cast<uint16_t*>(scales + gemm_scale_off(r, k, cols)) = (uint16_t)s2;
+            } else {
+                *reinterpret_cast<u32x4*>(codes + r * (cols >> 1) + gi * 16) = c;
+                *reinterpret_cast<uint16_t*>(scales + r * (cols >> 4) + gi * 2) = (uint16_t)s2;
+            }
+        }
+    }
+    if (lane == 0) gout[r] = rs.g;
+}
+
 }  // namespace nvfp4

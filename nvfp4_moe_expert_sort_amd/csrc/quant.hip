@@ -6,6 +6,8 @@
 // HBM-bound streaming kernels: each lane reads 64 contiguous bytes of one row
 // and writes 16 bytes of codes.
 //   quant_rows_kernel  one wave per row (generic entry point, weights, dense X);
+//                      rows of up to 8192 columns are read once into registers,
+//                      longer ones in two passes (amax, then quantize);
 //   quant_h_kernel     FC2 input: one wave per (32-row tile, 128 columns) of
 //                      the sorted buffer, writing whole 1 KiB GEMM chunks; the
 //                      row amax is the max of the per-32-column maxima the FC1
@@ -23,7 +25,17 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
                                                          int gemm, int round_up) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
-    quant_row_wave(x + row * ld, cols, -1.0f, round_up != 0, gemm != 0, row, codes, scales, g);
+    const uint16_t* xr = x + row * ld;
+    const bool ru = round_up != 0, gm = gemm != 0;
+    // Rows of up to 8192 columns (cols % 32 == 0) are read once into registers.
+    const int64_t per_lane = (cols % 32 == 0) ? (cols / 32 + kWave - 1) / kWave : 0;
+    switch (per_lane) {
+        case 1: quant_row_regs<1>(xr, cols, ru, gm, row, codes, scales, g); break;
+        case 2: quant_row_regs<2>(xr, cols, ru, gm, row, codes, scales, g); break;
+        case 3: quant_row_regs<3>(xr, cols, ru, gm, row, codes, scales, g); break;
+        case 4: quant_row_regs<4>(xr, cols, ru, gm, row, codes, scales, g); break;
+        default: quant_row_wave(xr, cols, -1.0f, ru, gm, row, codes, scales, g); break;
+    }
 }
 
 __global__ void __launch_bounds__(256) quant_h_kernel(const uint16_t* __restrict__ h, int64_t I,

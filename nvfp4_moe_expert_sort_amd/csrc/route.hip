@@ -28,41 +28,6 @@
 
 namespace nvfp4 {
 
-// One token row per wavefront, held in registers: lane l owns the 32-element
-// groups l, l + 64, ... (G of them), so the row is read once for its amax and
-// its quantization.  Same arithmetic as quant_row_wave (logical layout).
-template <int G>
-__device__ __forceinline__ void quant_row_regs(const uint16_t* __restrict__ x, int64_t cols, bool round_up, int64_t r,
-                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                               float* __restrict__ gout) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t groups = cols >> 5;  // cols % 32 == 0
-    u32x4 v[G][4];
-    uint32_t m = 0u;
-#pragma unroll
-    for (int g = 0; g < G; g++) {
-        const int64_t gi = lane + kWave * g;
-        if (gi < groups) {
-            load32(x + gi * 32, false, v[g]);
-            m = max(m, max(max(absmax8_bits(v[g][0]), absmax8_bits(v[g][1])),
-                           max(absmax8_bits(v[g][2]), absmax8_bits(v[g][3]))));
-        }
-    }
-    const RowScale rs = row_scale(bf16_to_f32(wave_max_u32(m)));
-#pragma unroll
-    for (int g = 0; g < G; g++) {
-        const int64_t gi = lane + kWave * g;
-        if (gi < groups) {
-            u32x4 c;
-            uint32_t s2;
-            quant32(v[g], rs, round_up, false, c, s2);
-            *reinterpret_cast<u32x4*>(codes + r * (cols >> 1) + gi * 16) = c;
-            *reinterpret_cast<uint16_t*>(scales + r * (cols >> 4) + gi * 2) = (uint16_t)s2;
-        }
-    }
-    if (lane == 0) gout[r] = rs.g;
-}
-
 constexpr int kCountThreads = kTokPerBlk * 64;  // one wavefront per token of the block
 
 __global__ void __launch_bounds__(kCountThreads) route_count_kernel(const uint16_t* __restrict__ x,
@@ -127,10 +92,10 @@ __global__ void __launch_bounds__(kCountThreads) route_count_kernel(const uint16
         const uint16_t* xr = x + t * H;
         const bool ru = round_up != 0;
         switch (groups_per_lane) {
-            case 1: quant_row_regs<1>(xr, H, ru, t, xq_codes, xq_scales, gx); break;
-            case 2: quant_row_regs<2>(xr, H, ru, t, xq_codes, xq_scales, gx); break;
-            case 3: quant_row_regs<3>(xr, H, ru, t, xq_codes, xq_scales, gx); break;
-            case 4: quant_row_regs<4>(xr, H, ru, t, xq_codes, xq_scales, gx); break;
+            case 1: quant_row_regs<1>(xr, H, ru, false, t, xq_codes, xq_scales, gx); break;
+            case 2: quant_row_regs<2>(xr, H, ru, false, t, xq_codes, xq_scales, gx); break;
+            case 3: quant_row_regs<3>(xr, H, ru, false, t, xq_codes, xq_scales, gx); break;
+            case 4: quant_row_regs<4>(xr, H, ru, false, t, xq_codes, xq_scales, gx); break;
             default: quant_row_wave(xr, H, -1.0f, ru, false, t, xq_codes, xq_scales, gx); break;
         }
     }
