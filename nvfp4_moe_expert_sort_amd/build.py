@@ -34,11 +34,28 @@ def _compile(src: str) -> str:
     return obj
 
 
+# Stand-alone measurement programs (not part of the library): the GEMM path
+# comparison behind the choice of exact f16 dequantization.
+PROBES = {"mfma_path_probe": os.path.join(HERE, "probes", "mfma_path.hip")}
+
+
+def _build_probe(item) -> str:
+    name, src = item
+    exe = os.path.join(os.path.dirname(LIB), name)
+    r = subprocess.run([hipcc(), *[f for f in HIPCC_FLAGS if f not in ("-fPIC", "-fvisibility=hidden")], src, "-o", exe],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    return exe
+
+
 def build(jobs: int = 6) -> str:
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(os.path.dirname(LIB), exist_ok=True)
     with ThreadPoolExecutor(max(1, jobs)) as ex:
+        probes = ex.map(_build_probe, PROBES.items())
         objs = list(ex.map(_compile, SOURCES))
+        list(probes)
     tmp = LIB + ".tmp"
     r = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
