@@ -249,9 +249,30 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
 #pragma unroll
                     for (int i = 0; i < NSUB; i++) acur[i] = anxt[i];
                 }
+                // The next step's activation fragments (loaded at this step's
+                // start, arrived by its second half) are decoded two per
+                // k-step behind the MFMAs of k-steps 4..7, into the other LDS
+                // buffer; the barrier at the step's end orders them before any
+                // reader.  On the last step they re-decode this step's codes
+                // into a buffer nobody reads, and a wave with no activation
+                // tile of its own (wave >= NSUB) decodes its clamped codes into
+                // an LDS slot no MFMA reads: no branch splits the MFMA stream.
+                if (st >= 4) {
+                    half2v sl, sh;
+                    if ((st - 4) < 2)
+                        scales_of<0>(nsa, sl, sh);
+                    else
+                        scales_of<1>(nsa, sl, sh);
+#pragma unroll
+                    for (int ff = 0; ff < 2; ff++) {
+                        const int f = 2 * (st - 4) + ff, fch = f >> 2, fks = f & 3;
+                        S.a[buf ^ 1][ai][fch][fks][lane] = decode8(na[fch][fks], fks < 2 ? sl : sh);
+                    }
+                }
             }
+        } else {
+            decode_a(buf ^ 1, na, nsa);
         }
-        if (more) decode_a(buf ^ 1, na, nsa);
         // Step cp+1's weight codes: landed in LDS (wait for this wave's
         // loads), into registers, then the slice is refilled for step cp+2.
         // On the last step this re-reads the slice; the values go unused.
