@@ -206,6 +206,10 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
         decode_a(0, ua, usa);
     }
     barrier_lds();
+    // Issue priority: the K loop's MFMA stream outranks a neighbouring
+    // wave's epilogue (VALU-heavy), so the two waves that share a SIMD keep
+    // its matrix pipe busy while one of them finishes a tile.
+    __builtin_amdgcn_s_setprio(2);
     for (int64_t cp = 0; cp < kc128; cp++) {
         const int buf = (int)(cp & 1);
         const bool more = cp + 1 < kc128;
@@ -289,6 +293,7 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
         }
         barrier_lds();
     }
+    __builtin_amdgcn_s_setprio(0);  // epilogue at the lowest priority
     if (!active) return;
 
     // Epilogue.  Lane l holds, for register r of an MFMA tile, row
