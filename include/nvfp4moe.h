@@ -175,8 +175,9 @@ NVFP4MOE_API int nvfp4moe_moe_expert_forward_events(const nvfp4moe_config* cfg, 
                                                     size_t workspace_bytes, void* const* events, void* stream);
 
 /* Device error word of the last forward that used `workspace`: 0 if clean,
- * else a bitwise OR of 1 (an id outside [0, E)) and 2 (an id repeated within a
- * token).  Syncs `stream`.  *code_host (host) receives the word. */
+ * else a bitwise OR of 1 (an id outside [0, E)), 2 (an id repeated within a
+ * token) and 4 (masked layout only: an expert received more pairs than its
+ * capacity).  Syncs `stream`.  *code_host (host) receives the word. */
 NVFP4MOE_API int nvfp4moe_device_error(const nvfp4moe_config* cfg, const void* workspace, int32_t* code_host, void* stream);
 
 /* Byte offsets of the forward's intermediates inside the workspace, for
@@ -193,12 +194,38 @@ typedef struct {
     size_t amax2_part;   /* float [rows_cap, n_part] max |h| of each 32-column group of h, per row */
     size_t a2_codes, a2_scales, a2_g;  /* quantized h, GEMM layout, rows_cap rows x I */
     size_t y2;           /* BF16 [rows_cap, H] FC2 output per sorted row */
-    int64_t rows_cap;    /* max_tokens*K + E*(m_align-1), rounded up to m_align */
+    int64_t rows_cap;    /* max_tokens*K + E*(m_align-1), rounded up to m_align (masked layout: E*capacity) */
     int32_t m_align;     /* each expert's rows are padded to a multiple of this */
     int32_t n_part;      /* I / 32: entries of amax2_part per row */
 } nvfp4moe_ws_layout;
 
 NVFP4MOE_API int nvfp4moe_workspace_layout(const nvfp4moe_config* cfg, nvfp4moe_ws_layout* layout_host);
+
+/* The masked fixed-capacity row layout (article, section 4.4, "two layouts,
+ * same row results": the decode side feeds the expert GEMMs per-expert chunks
+ * of a fixed capacity, the training side packed contiguous rows, and the
+ * same (token, slot) must get the same bits in both).  Expert e owns sorted
+ * rows [e*capacity, (e+1)*capacity): its pairs take rows e*capacity + i in
+ * the contiguous layout's order (i = the pair's rank within the expert), the
+ * rows up to the next multiple of m_align are padding, and the rest of the
+ * chunk is never read or written.  Every other rule of
+ * nvfp4moe_moe_expert_forward holds, and each pair's quantized rows, h, y2
+ * and each token's output are bitwise those of the contiguous layout.
+ *   capacity  rows per expert chunk: a positive multiple of m_align (32) with
+ *             E*capacity < 2^30, chosen by the caller independently of T
+ * A pair ranked >= capacity within its expert gets no row (pair2row -1, its
+ * term left out of its token's sum) and sets bit 4 of the device error word;
+ * the outputs of the tokens it belongs to are then unspecified.
+ * The workspace (bytes and layout from the _masked size functions, which
+ * return 0 / NVFP4_E_SHAPE for a bad capacity) holds E*capacity rows:
+ * rows_cap = E*capacity and off[e] = e*capacity, off[E] = E*capacity. */
+NVFP4MOE_API size_t nvfp4moe_workspace_bytes_masked(const nvfp4moe_config* cfg, int32_t capacity);
+NVFP4MOE_API int nvfp4moe_workspace_layout_masked(const nvfp4moe_config* cfg, int32_t capacity,
+                                                  nvfp4moe_ws_layout* layout_host);
+NVFP4MOE_API int nvfp4moe_moe_expert_forward_masked(const nvfp4moe_config* cfg, int32_t capacity, const uint16_t* x,
+                                                    int32_t T, const int32_t* ids, const float* probs,
+                                                    const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q, uint16_t* out,
+                                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Dense NVFP4 linear: out [M, N] = bf16((Q(x) . Wq^T) * g^x * g^w), with
  * x [M, K] BF16 and Wq one GEMM-layout matrix [N, K] (n_mats 1).  The

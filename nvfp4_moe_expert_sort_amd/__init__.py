@@ -25,7 +25,8 @@ LAYOUT_GEMM = 1
 EXPORTS = ["nvfp4_status_str", "nvfp4_quantize", "nvfp4moe_weight_bytes", "nvfp4moe_quantize_weights",
            "nvfp4moe_workspace_bytes", "nvfp4moe_moe_expert_forward", "nvfp4moe_moe_expert_forward_events",
            "nvfp4moe_device_error",
-           "nvfp4moe_workspace_layout", "nvfp4_linear_workspace_bytes", "nvfp4_linear",
+           "nvfp4moe_workspace_layout", "nvfp4moe_workspace_bytes_masked", "nvfp4moe_workspace_layout_masked",
+           "nvfp4moe_moe_expert_forward_masked", "nvfp4_linear_workspace_bytes", "nvfp4_linear",
            "nvfp4moe_selftest_batch_invariance"]
 
 
@@ -77,6 +78,9 @@ def lib():
                                                                ctypes.POINTER(vp), vp]),
         "nvfp4moe_device_error": (ctypes.c_int, [cfgp, vp, ctypes.POINTER(i32), vp]),
         "nvfp4moe_workspace_layout": (ctypes.c_int, [cfgp, ctypes.POINTER(WsLayout)]),
+        "nvfp4moe_workspace_bytes_masked": (sz, [cfgp, i32]),
+        "nvfp4moe_workspace_layout_masked": (ctypes.c_int, [cfgp, i32, ctypes.POINTER(WsLayout)]),
+        "nvfp4moe_moe_expert_forward_masked": (ctypes.c_int, [cfgp, i32, vp, i32, vp, vp, qtp, qtp, vp, vp, sz, vp]),
         "nvfp4_linear_workspace_bytes": (sz, [i64, i64]),
         "nvfp4_linear": (ctypes.c_int, [vp, i64, i64, qtp, vp, i32, vp, sz, vp]),
         "nvfp4moe_selftest_batch_invariance": (ctypes.c_int, [cfgp, qtp, qtp, ctypes.c_uint64, i32, i32, i32,
@@ -174,6 +178,40 @@ def workspace_layout(cfg: Config) -> WsLayout:
 def alloc_workspace(cfg: Config, device="cuda"):
     import torch
     return torch.empty((workspace_bytes(cfg),), dtype=torch.uint8, device=device)
+
+
+def workspace_bytes_masked(cfg: Config, capacity: int) -> int:
+    n = lib().nvfp4moe_workspace_bytes_masked(ctypes.byref(cfg), capacity)
+    if n == 0:
+        raise Nvfp4Error(2, "nvfp4moe_workspace_bytes_masked")
+    return n
+
+
+def workspace_layout_masked(cfg: Config, capacity: int) -> WsLayout:
+    out = WsLayout()
+    _check(lib().nvfp4moe_workspace_layout_masked(ctypes.byref(cfg), capacity, ctypes.byref(out)),
+           "nvfp4moe_workspace_layout_masked")
+    return out
+
+
+def alloc_workspace_masked(cfg: Config, capacity: int, device="cuda"):
+    import torch
+    return torch.empty((workspace_bytes_masked(cfg, capacity),), dtype=torch.uint8, device=device)
+
+
+def moe_expert_forward_masked(cfg: Config, capacity: int, x, ids, probs, weights: QuantWeights, workspace, out=None,
+                              stream=None):
+    """nvfp4moe_moe_expert_forward_masked: as moe_expert_forward, with expert e's rows in the fixed chunk
+    [e*capacity, (e+1)*capacity) of the workspace's sorted buffers."""
+    import torch
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, cfg.hidden), dtype=x.dtype, device=x.device)
+    st = lib().nvfp4moe_moe_expert_forward_masked(ctypes.byref(cfg), capacity, _ptr(x), T, _ptr(ids), _ptr(probs),
+                                                  ctypes.byref(weights.W1q), ctypes.byref(weights.W2q), _ptr(out),
+                                                  _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "nvfp4moe_moe_expert_forward_masked")
+    return out
 
 
 def moe_expert_forward(cfg: Config, x, ids, probs, weights: QuantWeights, workspace, out=None, stream=None):

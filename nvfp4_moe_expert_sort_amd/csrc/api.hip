@@ -44,11 +44,19 @@ struct Layout {
     size_t total;
 };
 
-Layout make_layout(const nvfp4moe_config* c) {
+// Masked layout: a positive multiple of kMAlign, with E * capacity rows
+// addressable by int32 row indices.
+bool capacity_ok(const nvfp4moe_config* c, int32_t capacity) {
+    return capacity > 0 && capacity % kMAlign == 0 && (int64_t)c->n_experts * capacity < ((int64_t)1 << 30);
+}
+
+// capacity 0: contiguous layout (rows bounded by max_tokens); > 0: masked
+// layout, E chunks of `capacity` rows.
+Layout make_layout(const nvfp4moe_config* c, int32_t capacity = 0) {
     Layout L{};
     const int64_t E = c->n_experts, K = c->top_k, H = c->hidden, I = c->inter, Tm = c->max_tokens;
     const int64_t P = Tm * K;
-    const int64_t rows = up((size_t)(P + E * (kMAlign - 1)), kMAlign);
+    const int64_t rows = capacity > 0 ? E * capacity : (int64_t)up((size_t)(P + E * (kMAlign - 1)), kMAlign);
     L.nblk_cap = std::max<int64_t>(1, (Tm + kTokPerBlk - 1) / kTokPerBlk);
     L.mtiles_cap = rows / kTileRows + E + 1;
     size_t o = 0;
@@ -179,6 +187,18 @@ int nvfp4moe_workspace_layout(const nvfp4moe_config* cfg, nvfp4moe_ws_layout* ou
     return NVFP4_OK;
 }
 
+size_t nvfp4moe_workspace_bytes_masked(const nvfp4moe_config* cfg, int32_t capacity) {
+    if (!cfg_ok(cfg) || !capacity_ok(cfg, capacity)) return 0;
+    return make_layout(cfg, capacity).total;
+}
+
+int nvfp4moe_workspace_layout_masked(const nvfp4moe_config* cfg, int32_t capacity, nvfp4moe_ws_layout* out) {
+    if (!cfg || !out) return NVFP4_E_NULL;
+    if (!cfg_ok(cfg) || !capacity_ok(cfg, capacity)) return NVFP4_E_SHAPE;
+    *out = make_layout(cfg, capacity).pub;
+    return NVFP4_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -186,18 +206,20 @@ namespace {
 // The forward; when `events` is non-null, events[i] is recorded on the stream
 // at each stage boundary (before the sort, after the sort, after FC1, after
 // the FC2-input quantizer, after FC2, after the combine).
+// capacity 0: the contiguous row layout; > 0: the masked layout.
 int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids, const float* probs,
                  const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q, uint16_t* out, void* workspace,
-                 size_t workspace_bytes, void* stream, void* const* events) {
+                 size_t workspace_bytes, void* stream, void* const* events, int32_t capacity = 0) {
     if (!cfg) return NVFP4_E_NULL;
     if (!cfg_ok(cfg)) return NVFP4_E_SHAPE;
+    if (capacity != 0 && !capacity_ok(cfg, capacity)) return NVFP4_E_SHAPE;
     if (T < 0) return NVFP4_E_SHAPE;
     if (T > cfg->max_tokens) return NVFP4_E_CAPACITY;
     const int64_t E = cfg->n_experts, K = cfg->top_k, H = cfg->hidden, I = cfg->inter;
     if (!W1q || !W2q) return NVFP4_E_NULL;
     if (!qt_ok(W1q, E, 2 * I, H) || !qt_ok(W2q, E, H, I)) return NVFP4_E_SHAPE;
     if (!workspace) return NVFP4_E_NULL;
-    const Layout L = make_layout(cfg);
+    const Layout L = make_layout(cfg, capacity);
     if (workspace_bytes < L.total) return NVFP4_E_WORKSPACE;
     if (!aligned(workspace, kAlign)) return NVFP4_E_ALIGN;
     if (T == 0) return NVFP4_OK;
@@ -229,7 +251,7 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     const bool ru = cfg->scale_round == NVFP4_SCALE_RU;
 
     if (!mark(0)) return NVFP4_E_HIP;
-    hipError_t e = launch_route(x, ids, probs, T, (int32_t)H, (int32_t)K, (int32_t)E, ru, rb, L.pub.rows_cap, s);
+    hipError_t e = launch_route(x, ids, probs, T, (int32_t)H, (int32_t)K, (int32_t)E, capacity, ru, rb, L.pub.rows_cap, s);
     if (e != hipSuccess || !mark(1)) return NVFP4_E_HIP;
 
     // Static bound on row tiles for this T (the device count is <= this).
@@ -261,9 +283,10 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     uint8_t* a2s = ws + L.pub.a2_scales;
     float* a2g = (float*)(ws + L.pub.a2_g);
     const int64_t rows_bound =
-        std::min<int64_t>(L.pub.rows_cap, ((int64_t)T * K + E * (kMAlign - 1) + kMAlign - 1) / kMAlign * kMAlign);
-    e = launch_quant_h(f1.out, rows_bound, I, rb.expert_off, (int32_t)E, rb.row2pair, f1.amax_part, f1.n_part, a2c,
-                       a2s, a2g, ru, s);
+        capacity > 0 ? L.pub.rows_cap
+                     : std::min<int64_t>(L.pub.rows_cap, ((int64_t)T * K + E * (kMAlign - 1) + kMAlign - 1) / kMAlign * kMAlign);
+    e = launch_quant_h(f1.out, rows_bound, I, rb.expert_off, (int32_t)E, capacity, rb.expert_count, rb.row2pair,
+                       f1.amax_part, f1.n_part, a2c, a2s, a2g, ru, s);
     if (e != hipSuccess || !mark(3)) return NVFP4_E_HIP;
 
     GemmParams f2{};
@@ -307,6 +330,14 @@ int nvfp4moe_moe_expert_forward_events(const nvfp4moe_config* cfg, const uint16_
     for (int i = 0; i < NVFP4MOE_N_STAGE_EVENTS; i++)
         if (!events[i]) return NVFP4_E_NULL;
     return forward_impl(cfg, x, T, ids, probs, W1q, W2q, out, workspace, workspace_bytes, stream, events);
+}
+
+int nvfp4moe_moe_expert_forward_masked(const nvfp4moe_config* cfg, int32_t capacity, const uint16_t* x, int32_t T,
+                                       const int32_t* ids, const float* probs, const nvfp4_qtensor* W1q,
+                                       const nvfp4_qtensor* W2q, uint16_t* out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    if (cfg && cfg_ok(cfg) && !capacity_ok(cfg, capacity)) return NVFP4_E_SHAPE;
+    return forward_impl(cfg, x, T, ids, probs, W1q, W2q, out, workspace, workspace_bytes, stream, nullptr, capacity);
 }
 
 int nvfp4moe_device_error(const nvfp4moe_config* cfg, const void* workspace, int32_t* code_host, void* stream) {

@@ -57,10 +57,31 @@ struct RouteBuffers {
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
                              uint8_t* scales, float* g, bool gemm, bool round_up, hipStream_t stream);
 hipError_t launch_quant_h(const uint16_t* h, int64_t rows_bound, int64_t I, const int32_t* expert_off, int32_t E,
-                          const int32_t* row2pair, const float* amax2_part, int n_part, uint8_t* codes,
-                          uint8_t* scales, float* g, bool round_up, hipStream_t stream);
+                          int32_t capacity, const int32_t* expert_count, const int32_t* row2pair,
+                          const float* amax2_part, int n_part, uint8_t* codes, uint8_t* scales, float* g,
+                          bool round_up, hipStream_t stream);
+// capacity 0: contiguous row layout; > 0: masked layout, expert e's rows in
+// the chunk [e * capacity, (e + 1) * capacity) (capacity % kMAlign == 0).
 hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* probs, int32_t T, int32_t H, int32_t K,
-                        int32_t E, bool round_up, const RouteBuffers& rb, int64_t rows_cap, hipStream_t stream);
+                        int32_t E, int32_t capacity, bool round_up, const RouteBuffers& rb, int64_t rows_cap,
+                        hipStream_t stream);
+
+#ifdef __HIPCC__
+// Whether the 32-row tile rt of the sorted buffers holds rows of an expert:
+// below off[E] in the contiguous layout (capacity 0); inside its expert's
+// padded rows in the masked layout (a chunk holds whole tiles, capacity being
+// a multiple of kMAlign).  Row tiles that hold none are never written.
+__device__ __forceinline__ bool row_tile_used(int64_t rt, int32_t E, int32_t capacity,
+                                              const int32_t* __restrict__ expert_off,
+                                              const int32_t* __restrict__ expert_count) {
+    const int64_t r = rt * kMAlign;
+    if (capacity <= 0) return r < expert_off[E];
+    const int64_t e = r / capacity;
+    if (e >= E) return false;
+    const int64_t kept = min(expert_count[e], capacity);
+    return r - e * capacity < (kept + kMAlign - 1) / kMAlign * kMAlign;
+}
+#endif
 int gemm_cols_per_tile(int mode);  // output columns per tile: 256 (plain) or 128 of h (128 gate + 128 up rows)
 hipError_t launch_gemm(int mode, const GemmParams& P, int grid_blocks, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* y2, const int32_t* pair2row, int32_t T, int32_t H, int32_t K,

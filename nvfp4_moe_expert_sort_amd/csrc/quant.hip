@@ -43,6 +43,7 @@ constexpr int kQuantHSteps = 1;
 
 __global__ void __launch_bounds__(256) quant_h_kernel(const uint16_t* __restrict__ h, int64_t I,
                                                       const int32_t* __restrict__ expert_off, int32_t E,
+                                                      int32_t capacity, const int32_t* __restrict__ expert_count,
                                                       const int32_t* __restrict__ row2pair,
                                                       const float* __restrict__ amax2_part, int n_part,
                                                       int64_t n_units, uint8_t* __restrict__ codes,
@@ -53,7 +54,7 @@ __global__ void __launch_bounds__(256) quant_h_kernel(const uint16_t* __restrict
     if (unit >= n_units) return;
     const int64_t cps = I / 128, groups = (cps + kQuantHSteps - 1) / kQuantHSteps;
     const int64_t rt = unit / groups, cp0 = (unit % groups) * kQuantHSteps;
-    if (rt * 32 >= expert_off[E]) return;  // past the last expert's rows
+    if (!row_tile_used(rt, E, capacity, expert_off, expert_count)) return;
     const int hh = lane >> 5, rl = lane & 31;
     const int64_t row = rt * 32 + rl;
     const bool valid = row2pair[row] >= 0;  // padding rows are written as zeros
@@ -105,12 +106,13 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
 }
 
 hipError_t launch_quant_h(const uint16_t* h, int64_t rows_bound, int64_t I, const int32_t* expert_off, int32_t E,
-                          const int32_t* row2pair, const float* amax2_part, int n_part, uint8_t* codes,
-                          uint8_t* scales, float* g, bool round_up, hipStream_t stream) {
+                          int32_t capacity, const int32_t* expert_count, const int32_t* row2pair,
+                          const float* amax2_part, int n_part, uint8_t* codes, uint8_t* scales, float* g,
+                          bool round_up, hipStream_t stream) {
     const int64_t n_units = rows_bound / 32 * ((I / 128 + kQuantHSteps - 1) / kQuantHSteps);
     if (n_units <= 0) return hipSuccess;
     hipLaunchKernelGGL(quant_h_kernel, dim3((unsigned)((n_units + 3) / 4)), dim3(256), 0, stream, h, I, expert_off, E,
-                       row2pair, amax2_part, n_part, n_units, codes, scales, g, round_up ? 1 : 0);
+                       capacity, expert_count, row2pair, amax2_part, n_part, n_units, codes, scales, g, round_up ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -20,6 +20,15 @@
 //                 chunks; padding rows are written as zeros.
 // Integer atomics only on LDS counters: every count and row index is
 // independent of scheduling.
+//
+// Two row layouts (article section 4.4, "two layouts, same row results"):
+// contiguous (capacity 0), where expert e's rows start at the padded prefix
+// of the counts before it, and masked, where every expert owns a fixed chunk
+// of `capacity` rows starting at e * capacity and the chunk's rows past the
+// expert's padded count are never touched.  A row's content does not depend
+// on where it sits, so both give the same bits per (token, slot).  Pairs
+// ranked past the capacity of their expert get no row and raise bit 4 of the
+// error word.
 #include <algorithm>
 
 #include "nvfp4_device.h"
@@ -140,7 +149,8 @@ __device__ int2 block_scan_incl2(int2 v, int2* wsum /* [16] */) {
 
 constexpr int kScanRegs = 32;  // block counts a scan thread keeps in registers
 
-__global__ void __launch_bounds__(1024) route_scan_kernel(int32_t nblk, int32_t E, int32_t* __restrict__ blk_counts,
+__global__ void __launch_bounds__(1024) route_scan_kernel(int32_t nblk, int32_t E, int32_t capacity,
+                                                          int32_t* __restrict__ blk_counts,
                                                           const int32_t* __restrict__ blk_err,
                                                           int32_t* __restrict__ expert_count,
                                                           int32_t* __restrict__ expert_off,
@@ -192,38 +202,42 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(int32_t nblk, int32_t 
             }
         }
     }
-    // (2) totals, padded offsets and row-tile counts per expert (thread e).
-    int32_t cnt = 0, padded = 0, ntile = 0;
+    // (2) totals, padded offsets and row-tile counts per expert (thread e);
+    //     in the masked layout an expert keeps at most `capacity` rows.
+    int32_t cnt = 0, kept = 0, padded = 0, ntile = 0;
     if (tid < E) {
         for (int s = 0; s < tpe; s++) cnt += part[tid * tpe + s];
-        padded = (cnt + kMAlign - 1) / kMAlign * kMAlign;
+        kept = capacity > 0 ? min(cnt, capacity) : cnt;
+        padded = (kept + kMAlign - 1) / kMAlign * kMAlign;
         ntile = (padded + kTileRows - 1) / kTileRows;
+        if (kept < cnt) atomicOr(&errs, 4);
     }
     const int2 incl = block_scan_incl2(make_int2(padded, ntile), wsum);
     if (tid < E) {
-        const int32_t off = incl.x - padded;
+        const int32_t off = capacity > 0 ? tid * capacity : incl.x - padded;
         const int32_t t0 = incl.y - ntile;
         expert_count[tid] = cnt;
         expert_off[tid] = off;
         if (tid == E - 1) {
-            expert_off[E] = incl.x;
+            expert_off[E] = capacity > 0 ? E * capacity : incl.x;
             *n_mtiles = incl.y;
-            *err_word = errs;
         }
         for (int i = 0; i < ntile; i++) {
             const int32_t r0 = off + i * kTileRows;
             const int32_t nsub = min(kTileRows, padded - i * kTileRows) / kMAlign;
-            mtiles[t0 + i] = make_int4(r0, tid, nsub, off + cnt);
+            mtiles[t0 + i] = make_int4(r0, tid, nsub, off + kept);
         }
-        for (int r = off + cnt; r < off + padded; r++) row2pair[r] = -1;
+        for (int r = off + kept; r < off + padded; r++) row2pair[r] = -1;
     }
+    __syncthreads();  // every expert's overflow bit is in
+    if (tid == 0) *err_word = errs;
 }
 
 // pair2row[p] holds the pair's rank within (its block, its expert) on entry
 // and its sorted row on exit.
 __global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restrict__ ids,
                                                           const float* __restrict__ probs, int64_t P, int32_t K,
-                                                          int32_t E, const int32_t* __restrict__ blk_base,
+                                                          int32_t E, int32_t capacity, const int32_t* __restrict__ blk_base,
                                                           const int32_t* __restrict__ expert_off, int32_t* pair2row,
                                                           int32_t* __restrict__ row2pair, float* __restrict__ row_prob) {
     const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -234,8 +248,12 @@ __global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restr
         return;
     }
     const int64_t blk = (p / K) / kTokPerBlk;
-    const int32_t rank = pair2row[p];
-    const int32_t row = expert_off[e] + blk_base[blk * E + e] + rank;
+    const int32_t local = blk_base[blk * E + e] + pair2row[p];  // rank within the expert
+    if (capacity > 0 && local >= capacity) {  // past the expert's chunk (error bit 4)
+        pair2row[p] = -1;
+        return;
+    }
+    const int32_t row = expert_off[e] + local;
     pair2row[p] = row;
     row2pair[row] = (int32_t)p;
     row_prob[row] = probs[p];
@@ -248,7 +266,9 @@ constexpr int kGatherSteps = 2;  // 128-column steps per gather wave
 // each chunk c from its token's quantized row, so every chunk is written as
 // one contiguous 1 KiB; all loads are issued before the stores.
 __global__ void __launch_bounds__(256) route_gather_kernel(int32_t H, int32_t K, const int32_t* __restrict__ expert_off,
-                                                           int32_t E, const int32_t* __restrict__ row2pair,
+                                                           int32_t E, int32_t capacity,
+                                                           const int32_t* __restrict__ expert_count,
+                                                           const int32_t* __restrict__ row2pair,
                                                            const uint8_t* __restrict__ xq_codes,
                                                            const uint8_t* __restrict__ xq_scales,
                                                            const float* __restrict__ gx, int64_t n_units,
@@ -259,7 +279,7 @@ __global__ void __launch_bounds__(256) route_gather_kernel(int32_t H, int32_t K,
     if (unit >= n_units) return;
     const int64_t cps = H / 128, groups = (cps + kGatherSteps - 1) / kGatherSteps;
     const int64_t rt = unit / groups, cp0 = (unit % groups) * kGatherSteps;
-    if (rt * 32 >= expert_off[E]) return;  // past the last expert's rows
+    if (!row_tile_used(rt, E, capacity, expert_off, expert_count)) return;
     const int h = lane >> 5, rl = lane & 31;
     const int64_t row = rt * 32 + rl;
     const int32_t p = row2pair[row];
@@ -293,27 +313,29 @@ __global__ void __launch_bounds__(256) route_gather_kernel(int32_t H, int32_t K,
 }
 
 hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* probs, int32_t T, int32_t H, int32_t K,
-                        int32_t E, bool round_up, const RouteBuffers& rb, int64_t rows_cap, hipStream_t stream) {
+                        int32_t E, int32_t capacity, bool round_up, const RouteBuffers& rb, int64_t rows_cap,
+                        hipStream_t stream) {
     const int32_t nblk = (T + kTokPerBlk - 1) / kTokPerBlk;
     hipLaunchKernelGGL(route_count_kernel, dim3(nblk), dim3(kCountThreads), 0, stream, x, ids, T, H, K, E, round_up ? 1 : 0,
                        rb.blk_counts, rb.blk_err, rb.pair2row /* holds the ranks until route_place */, rb.xq_codes,
                        rb.xq_scales, rb.gx);
     hipError_t st = hipGetLastError();
     if (st != hipSuccess) return st;
-    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, nblk, E, rb.blk_counts, rb.blk_err,
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, nblk, E, capacity, rb.blk_counts, rb.blk_err,
                        rb.expert_count, rb.expert_off, rb.mtiles, rb.n_mtiles, rb.row2pair, rb.err_word);
     st = hipGetLastError();
     if (st != hipSuccess) return st;
     const int64_t P = (int64_t)T * K;
     hipLaunchKernelGGL(route_place_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, stream, ids, probs, P, K, E,
-                       rb.blk_counts, rb.expert_off, rb.pair2row, rb.row2pair, rb.row_prob);
+                       capacity, rb.blk_counts, rb.expert_off, rb.pair2row, rb.row2pair, rb.row_prob);
     st = hipGetLastError();
     if (st != hipSuccess) return st;
     // Row tiles that can hold rows for this T (the device offsets decide which are used).
-    const int64_t rows_bound = std::min<int64_t>(rows_cap, (P + (int64_t)E * (kMAlign - 1) + 31) / 32 * 32);
+    const int64_t rows_bound =
+        capacity > 0 ? rows_cap : std::min<int64_t>(rows_cap, (P + (int64_t)E * (kMAlign - 1) + 31) / 32 * 32);
     const int64_t n_units = rows_bound / 32 * ((H / 128 + kGatherSteps - 1) / kGatherSteps);
     hipLaunchKernelGGL(route_gather_kernel, dim3((unsigned)((n_units + 3) / 4)), dim3(256), 0, stream, H, K,
-                       rb.expert_off, E, rb.row2pair, rb.xq_codes, rb.xq_scales, rb.gx, n_units, rb.a_codes,
+                       rb.expert_off, E, capacity, rb.expert_count, rb.row2pair, rb.xq_codes, rb.xq_scales, rb.gx, n_units, rb.a_codes,
                        rb.a_scales, rb.a_g);
     return hipGetLastError();
 }

@@ -112,6 +112,38 @@ def test_forward_host_validation(m):
     assert f(ctypes.byref(cfg), None, 0, None, None, ctypes.byref(W1), ctypes.byref(W2), None, fake, need, None) == 0
 
 
+def test_masked_layout_sizes_and_host_validation(m):
+    """Masked fixed-capacity layout: E chunks of `capacity` rows (a positive
+    multiple of 32), checked on the host before anything is launched."""
+    lib = m.lib()
+    cfg = _cfg(m, max_tokens=64)
+    E, H, I = 128, 2048, 768
+    for bad in (0, -32, 16, 33, 1 << 23):  # 1 << 23 rows per expert: E * capacity >= 2**30
+        assert lib.nvfp4moe_workspace_bytes_masked(ctypes.byref(cfg), bad) == 0
+        lay = m.WsLayout()
+        assert lib.nvfp4moe_workspace_layout_masked(ctypes.byref(cfg), bad, ctypes.byref(lay)) == 2
+    lay = m.workspace_layout_masked(cfg, 96)
+    assert lay.rows_cap == E * 96 and lay.m_align == 32
+    offs = [lay.err, lay.expert_count, lay.expert_off, lay.pair2row, lay.row2pair, lay.a1_codes, lay.a1_scales,
+            lay.a1_g, lay.h, lay.amax2_part, lay.a2_codes, lay.a2_scales, lay.a2_g, lay.y2]
+    need = m.workspace_bytes_masked(cfg, 96)
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs) and offs[-1] < need
+    # the chunks, not max_tokens, size the row buffers
+    assert m.workspace_bytes_masked(cfg, 192) > need
+    assert m.workspace_layout_masked(_cfg(m, max_tokens=4096), 96).rows_cap == E * 96
+    f = lib.nvfp4moe_moe_expert_forward_masked
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    W1 = m.QTensor(0x1000, 0x1000, 0x1000, E, 2 * I, H, m.LAYOUT_GEMM)
+    W2 = m.QTensor(0x1000, 0x1000, 0x1000, E, H, I, m.LAYOUT_GEMM)
+    args = lambda cap, T, ws_bytes: (ctypes.byref(cfg), cap, fake, T, fake, fake, ctypes.byref(W1), ctypes.byref(W2),
+                                     fake, fake, ws_bytes, None)
+    assert f(*args(48, 1, need)) == 2     # capacity not a multiple of 32
+    assert f(*args(96, 65, need)) == 5    # T > max_tokens
+    assert f(*args(96, 1, need - 1)) == 4  # workspace sized for this capacity
+    assert f(*args(192, 1, need)) == 4    # a larger capacity needs a larger workspace
+    assert f(*args(96, 0, need)) == 0     # T == 0: no-op
+
+
 def test_quantize_host_validation(m):
     q = m.lib().nvfp4_quantize
     fake = ctypes.c_void_p(0x1000)
