@@ -83,6 +83,10 @@ def _load():
     lib.orc_combine.argtypes = [P, I64, I64, I64, P]
     lib.orc_route.restype = I64
     lib.orc_route.argtypes = [P, I64, I64, I64, I64, P, P, P, I64]
+    lib.orc_router_logits.restype = None
+    lib.orc_router_logits.argtypes = [P, I64, I64, P, I64, P]
+    lib.orc_router_topk.restype = None
+    lib.orc_router_topk.argtypes = [P, I64, I64, I64, ctypes.c_int, P, P]
     lib.orc_moe_forward_deq.restype = None
     lib.orc_moe_forward_deq.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P, P, ctypes.c_int, P, P, P, P, P]
     lib.orc_moe_forward.restype = None
@@ -219,6 +223,31 @@ def route(ids: np.ndarray, n_experts: int, m_align: int):
     if P_pad < 0:
         raise ValueError("expert id out of range")
     return off, pair2row, row2pair[:P_pad].copy()
+
+
+def router_logits(x_bf16: np.ndarray, w_bf16: np.ndarray) -> np.ndarray:
+    """Router scores x . w^T of BF16 x [T, H] and w [E, H], exact in FP64 (article,
+    section 4.4, "R3 unnecessary": one FP32-output scoring kernel for every batch size)."""
+    x = _c(x_bf16, np.uint16)
+    w = _c(w_bf16, np.uint16)
+    T, H = x.shape
+    E = w.shape[0]
+    assert w.shape[1] == H
+    out = np.empty((T, E), np.float64)
+    _load().orc_router_logits(_p(x), T, H, _p(w), E, _p(out))
+    return out
+
+
+def router_topk(logits_f32: np.ndarray, k: int, renormalize: bool = True):
+    """Top-k of FP32 router scores: higher score first, equal scores to the lower
+    expert id (article, section 2: same tie-breaking and output order); softmax
+    probabilities over the k selected (renormalize) or all experts, FP64 -> FP32."""
+    l = _c(logits_f32, np.float32)
+    T, E = l.shape
+    ids = np.empty((T, k), np.int32)
+    probs = np.empty((T, k), np.float32)
+    _load().orc_router_topk(_p(l), T, E, k, 1 if renormalize else 0, _p(ids), _p(probs))
+    return ids, probs
 
 
 class DequantWeights:

@@ -331,6 +331,55 @@ int64_t orc_route(const int32_t* ids, int64_t T, int64_t K, int64_t E, int64_t m
 }
 
 /* ------------------------------------------------------------------------ */
+/* Router (the step before the path)                                         */
+/* ------------------------------------------------------------------------ */
+
+/* Router scores: logits[t][e] = sum_h x[t][h] * w[e][h] over the BF16 values,
+ * in FP64 (every product of two BF16 values is exact in FP64).  The article,
+ * section 4.4 ("R3 unnecessary"): the scoring GEMM is one FP32-output kernel
+ * for every batch size; this is the exact value that kernel approximates. */
+void orc_router_logits(const uint16_t* x, int64_t T, int64_t H, const uint16_t* w, int64_t E, double* logits) {
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t e = 0; e < E; e++) {
+            double acc = 0.0;
+            for (int64_t h = 0; h < H; h++) acc += orc_bf16_to_double(x[t * H + h]) * orc_bf16_to_double(w[e * H + h]);
+            logits[t * E + e] = acc;
+        }
+}
+
+/* Top-k of given FP32 router scores (the article, section 2: the same
+ * discrete choice needs the same tie-breaking and output order).  Experts are
+ * ranked by score, higher first, equal scores by the lower expert id: a total
+ * order, so the K selected and their order are unique.  Slot k holds the k-th
+ * expert of that order.  Probabilities (softmax; the softmax is increasing in
+ * the score, so it selects the same experts): p_k = exp(l_k - l_0) / D with D
+ * the sum of exp(l_j - l_0) over the K selected (renormalize != 0) or over
+ * all E experts, in FP64, stored as FP32. */
+void orc_router_topk(const float* logits, int64_t T, int64_t E, int64_t K, int renormalize, int32_t* ids,
+                     float* probs) {
+    char* taken = (char*)malloc((size_t)E);
+    for (int64_t t = 0; t < T; t++) {
+        const float* l = logits + t * E;
+        memset(taken, 0, (size_t)E);
+        for (int64_t k = 0; k < K; k++) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; e++) /* strict '>' keeps the lower id on equal scores */
+                if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;
+            taken[best] = 1;
+            ids[t * K + k] = (int32_t)best;
+        }
+        const double top = l[ids[t * K]];
+        double den = 0.0;
+        if (renormalize)
+            for (int64_t k = 0; k < K; k++) den += exp((double)l[ids[t * K + k]] - top);
+        else
+            for (int64_t e = 0; e < E; e++) den += exp((double)l[e] - top);
+        for (int64_t k = 0; k < K; k++) probs[t * K + k] = (float)(exp((double)l[ids[t * K + k]] - top) / den);
+    }
+    free(taken);
+}
+
+/* ------------------------------------------------------------------------ */
 /* The layer                                                                 */
 /* ------------------------------------------------------------------------ */
 
