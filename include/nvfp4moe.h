@@ -227,6 +227,27 @@ NVFP4MOE_API int nvfp4moe_moe_expert_forward_masked(const nvfp4moe_config* cfg, 
                                                     const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q, uint16_t* out,
                                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Router: the step that produces ids and probs for the expert forward.
+ * Article, section 4.4 ("R3 unnecessary": the scoring GEMM is one
+ * FP32-output kernel for every batch size, so routing recomputed on another
+ * side matches) and section 2 (the same discrete choice needs the same
+ * tie-breaking and output order).
+ *   x         [T, H] BF16 tokens; w_router [E, H] BF16 (16-byte aligned)
+ *   logits    [T, E] FP32 out: sum_h x[t,h] * w[e,h], accumulated in FP32
+ *             by one instruction sequence for every T and every position of
+ *             the token in the batch (bitwise batch-invariant)
+ *   ids       [T, K] int32 out: the K highest-scoring experts, higher score
+ *             first, equal scores (-0 equals +0) to the lower expert id
+ *   probs     [T, K] FP32 out: exp(l_k - l_0) / D, with D the FP32 sum of
+ *             exp(l_j - l_0) over the K selected in slot order (renormalize
+ *             1) or over all E experts (renormalize 0)
+ * Requirements: H % 16 == 0, 1 <= E <= 1024, 1 <= K <= min(E, 32);
+ * T == 0 is a no-op.  NaN scores are outside the contract.  The outputs are
+ * the caller's buffers; no workspace, no synchronisation. */
+NVFP4MOE_API int nvfp4moe_router_topk(const uint16_t* x, int32_t T, int32_t H, const uint16_t* w_router, int32_t E,
+                                      int32_t K, int32_t renormalize, float* logits, int32_t* ids, float* probs,
+                                      void* stream);
+
 /* Dense NVFP4 linear: out [M, N] = bf16((Q(x) . Wq^T) * g^x * g^w), with
  * x [M, K] BF16 and Wq one GEMM-layout matrix [N, K] (n_mats 1).  The
  * activation quantization uses scale_round.  M >= 0, K % 128 == 0,

@@ -26,7 +26,7 @@ EXPORTS = ["nvfp4_status_str", "nvfp4_quantize", "nvfp4moe_weight_bytes", "nvfp4
            "nvfp4moe_workspace_bytes", "nvfp4moe_moe_expert_forward", "nvfp4moe_moe_expert_forward_events",
            "nvfp4moe_device_error",
            "nvfp4moe_workspace_layout", "nvfp4moe_workspace_bytes_masked", "nvfp4moe_workspace_layout_masked",
-           "nvfp4moe_moe_expert_forward_masked", "nvfp4_linear_workspace_bytes", "nvfp4_linear",
+           "nvfp4moe_moe_expert_forward_masked", "nvfp4moe_router_topk", "nvfp4_linear_workspace_bytes", "nvfp4_linear",
            "nvfp4moe_selftest_batch_invariance"]
 
 
@@ -81,6 +81,7 @@ def lib():
         "nvfp4moe_workspace_bytes_masked": (sz, [cfgp, i32]),
         "nvfp4moe_workspace_layout_masked": (ctypes.c_int, [cfgp, i32, ctypes.POINTER(WsLayout)]),
         "nvfp4moe_moe_expert_forward_masked": (ctypes.c_int, [cfgp, i32, vp, i32, vp, vp, qtp, qtp, vp, vp, sz, vp]),
+        "nvfp4moe_router_topk": (ctypes.c_int, [vp, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp]),
         "nvfp4_linear_workspace_bytes": (sz, [i64, i64]),
         "nvfp4_linear": (ctypes.c_int, [vp, i64, i64, qtp, vp, i32, vp, sz, vp]),
         "nvfp4moe_selftest_batch_invariance": (ctypes.c_int, [cfgp, qtp, qtp, ctypes.c_uint64, i32, i32, i32,
@@ -248,6 +249,21 @@ def device_error(cfg: Config, workspace, stream=None) -> int:
     _check(lib().nvfp4moe_device_error(ctypes.byref(cfg), _ptr(workspace), ctypes.byref(code), _stream(stream)),
            "nvfp4moe_device_error")
     return code.value
+
+
+def router_topk(x, w_router, k: int, renormalize: bool = True, stream=None):
+    """nvfp4moe_router_topk: x [T,H] BF16, w_router [E,H] BF16 -> (logits [T,E] f32, ids [T,k] int32,
+    probs [T,k] f32)."""
+    import torch
+    T, H = x.shape
+    E = w_router.shape[0]
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    probs = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    st = lib().nvfp4moe_router_topk(_ptr(x), T, H, _ptr(w_router), E, k, 1 if renormalize else 0, _ptr(logits),
+                                    _ptr(ids), _ptr(probs), _stream(stream))
+    _check(st, "nvfp4moe_router_topk")
+    return logits, ids, probs
 
 
 def linear_workspace_bytes(M: int, K: int) -> int:

@@ -353,6 +353,20 @@ int nvfp4moe_device_error(const nvfp4moe_config* cfg, const void* workspace, int
     return NVFP4_OK;
 }
 
+int nvfp4moe_router_topk(const uint16_t* x, int32_t T, int32_t H, const uint16_t* w_router, int32_t E, int32_t K,
+                         int32_t renormalize, float* logits, int32_t* ids, float* probs, void* stream) {
+    if (T < 0 || H <= 0 || H % 16 != 0 || E < 1 || E > kMaxExperts || K < 1 || K > E || K > kMaxTopK)
+        return NVFP4_E_SHAPE;
+    if ((int64_t)T * std::max(H, E) >= ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
+    if (renormalize != 0 && renormalize != 1) return NVFP4_E_ARG;
+    if (T == 0) return NVFP4_OK;
+    if (!x || !w_router || !logits || !ids || !probs) return NVFP4_E_NULL;
+    if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(logits, 4) || !aligned(ids, 4) || !aligned(probs, 4))
+        return NVFP4_E_ALIGN;
+    return hip_status(launch_router(x, T, H, w_router, E, K, renormalize != 0, logits, ids, probs,
+                                    (hipStream_t)stream));
+}
+
 size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K) {
     if (M < 0 || K <= 0 || K % 128 != 0) return 0;
     const size_t rows = up((size_t)std::max<int64_t>(M, 1), 32);

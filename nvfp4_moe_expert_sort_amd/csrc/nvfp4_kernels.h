@@ -66,6 +66,10 @@ hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* prob
                         int32_t E, int32_t capacity, bool round_up, const RouteBuffers& rb, int64_t rows_cap,
                         hipStream_t stream);
 
+// Router scores logits [T, E] (FP32) and the top-K ids / probabilities per token.
+hipError_t launch_router(const uint16_t* x, int32_t T, int32_t H, const uint16_t* w, int32_t E, int32_t K,
+                         bool renorm, float* logits, int32_t* ids, float* probs, hipStream_t stream);
+
 #ifdef __HIPCC__
 // Whether the 32-row tile rt of the sorted buffers holds rows of an expert:
 // below off[E] in the contiguous layout (capacity 0); inside its expert's

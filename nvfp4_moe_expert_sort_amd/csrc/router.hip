@@ -1,0 +1,150 @@
+// router.hip -- router scores and deterministic top-k: the step that produces
+// the expert ids and probabilities the expert forward takes.
+//
+// Article "Finish RL training faster: bitwise consistent, high-performance,
+// agent-driven": section 4.4 ("R3 unnecessary": the scoring GEMM is one
+// FP32-output kernel for every batch size, so routing recomputed on the
+// training side matches the rollout) and section 2 (the same discrete choice
+// needs the same tie-breaking and output order).
+//
+// One launch, one workgroup per 32 tokens:
+//   phase 1  logits[t][e] = sum_h x[t][h] w[e][h]: BF16 MFMA 32x32x16 with
+//            FP32 accumulation, one 32-expert tile per wave at a time, the
+//            full H in one fixed order, fragments loaded straight from
+//            memory (16 contiguous bytes per lane).  A token's scores come
+//            from the same instruction sequence whatever T is and wherever
+//            the token sits in its tile.
+//   phase 2  per token (one wavefront): K rounds of a wave-wide maximum of
+//            64-bit keys (order-preserving score bits, then the complement of
+//            the expert id, so equal scores go to the lower id); slot k gets
+//            the k-th expert of that total order.  Probabilities are the
+//            softmax restricted to the selection (renormalize) or over all
+//            experts, in FP32 with one fixed summation order.
+#include "nvfp4_device.h"
+#include "nvfp4_kernels.h"
+
+namespace nvfp4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kRouterTok = 32;                        // tokens per workgroup (one MFMA row tile)
+constexpr int kRouterKeys = kMaxExperts / kWave;      // scores per lane in phase 2
+
+// Unsigned integer whose order is the order of the FP32 value (-0 and +0 equal).
+__device__ __forceinline__ uint32_t score_order(float v) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float score_value(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__global__ void __launch_bounds__(256) router_kernel(const uint16_t* __restrict__ x, int32_t T, int32_t H,
+                                                     const uint16_t* __restrict__ w, int32_t E, int32_t K,
+                                                     int renorm, float* __restrict__ logits,
+                                                     int32_t* __restrict__ ids, float* __restrict__ probs) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t0 = (int64_t)blockIdx.x * kRouterTok;
+
+    // Phase 1.  MFMA operands: lane (kh*32 + r) supplies row r of the token
+    // tile (A) and of the expert tile (B), k = 8 kh .. 8 kh + 7 of the step.
+    const int r = lane & 31, kh = lane >> 5;
+    const int64_t tok = min(t0 + r, (int64_t)T - 1);  // rows past T read the last token, not stored
+    const uint16_t* xa = x + tok * H + 8 * kh;
+    for (int nt = wave; nt * 32 < E; nt += 4) {
+        const int64_t e = min(nt * 32 + r, E - 1);  // columns past E read the last expert, not stored
+        const uint16_t* wb = w + e * H + 8 * kh;
+        f32x16 acc = {};
+        // k-steps of 16 in groups of four, their loads issued together; the
+        // MFMAs run in increasing k either way
+        int k = 0;
+        for (; k + 64 <= H; k += 64) {
+            u32x4 a[4], b[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                a[q] = *reinterpret_cast<const u32x4*>(xa + k + 16 * q);
+                b[q] = *reinterpret_cast<const u32x4*>(wb + k + 16 * q);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[q]),
+                                                              __builtin_bit_cast(bf16x8, b[q]), acc, 0, 0, 0);
+        }
+        for (; k < H; k += 16) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xa + k));
+            const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wb + k));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+        }
+        // register j: row (j/4)*8 + kh*4 + j%4 of the token tile, column r
+        const int col = nt * 32 + r;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            const int64_t t = t0 + (j >> 2) * 8 + kh * 4 + (j & 3);
+            if (t < T && col < E) logits[t * E + col] = acc[j];
+        }
+    }
+    __syncthreads();  // this workgroup's scores are written (workgroup-scope fence included)
+
+    // Phase 2: wave w takes tokens w, w + 4, ... of the tile.
+    for (int tl = wave; tl < kRouterTok; tl += 4) {
+        const int64_t t = t0 + tl;
+        if (t >= T) break;
+        const float* lt = logits + t * E;
+        uint64_t key[kRouterKeys];
+#pragma unroll
+        for (int i = 0; i < kRouterKeys; i++) {
+            const int e = i * kWave + lane;
+            key[i] = e < E ? ((uint64_t)score_order(lt[e]) << 32) | (uint32_t)~(uint32_t)e : 0ull;
+        }
+        int my_e = 0;
+        float my_l = 0.0f;
+        for (int k = 0; k < K; k++) {
+            uint64_t best = 0ull;
+#pragma unroll
+            for (int i = 0; i < kRouterKeys; i++) best = key[i] > best ? key[i] : best;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const uint64_t u = __shfl_xor(best, o, kWave);
+                best = u > best ? u : best;
+            }
+#pragma unroll
+            for (int i = 0; i < kRouterKeys; i++)
+                if (key[i] == best) key[i] = 0ull;  // keys are unique: one owner
+            if (lane == k) {
+                my_e = (int)~(uint32_t)best;
+                my_l = score_value((uint32_t)(best >> 32));
+            }
+        }
+        const float top = __shfl(my_l, 0, kWave);
+        const float num = lane < K ? expf(my_l - top) : 0.0f;
+        float den = 0.0f;
+        if (renorm) {
+            for (int k = 0; k < K; k++) den += __shfl(num, k, kWave);  // slot order
+        } else {
+            // this lane's experts in increasing order, then a fixed butterfly
+#pragma unroll
+            for (int i = 0; i < kRouterKeys; i++) {
+                const int e = i * kWave + lane;
+                if (e < E) den += expf(lt[e] - top);
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, kWave);
+        }
+        if (lane < K) {
+            ids[t * K + lane] = my_e;
+            probs[t * K + lane] = num / den;
+        }
+    }
+}
+
+hipError_t launch_router(const uint16_t* x, int32_t T, int32_t H, const uint16_t* w, int32_t E, int32_t K,
+                         bool renorm, float* logits, int32_t* ids, float* probs, hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((T + kRouterTok - 1) / kRouterTok);
+    hipLaunchKernelGGL(router_kernel, dim3(blocks), dim3(256), 0, stream, x, T, H, w, E, K, renorm ? 1 : 0, logits,
+                       ids, probs);
+    return hipGetLastError();
+}
+
+}  // namespace nvfp4

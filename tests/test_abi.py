@@ -144,6 +144,24 @@ def test_masked_layout_sizes_and_host_validation(m):
     assert f(*args(96, 0, need)) == 0     # T == 0: no-op
 
 
+def test_router_host_validation(m):
+    f = m.lib().nvfp4moe_router_topk
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    ok = dict(T=4, H=256, E=64, K=8, renorm=1)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(fake, a["T"], a["H"], fake, a["E"], a["K"], a["renorm"], fake, fake, fake, None)
+    assert call(H=200) == 2 and call(H=0) == 2          # H % 16
+    assert call(E=0) == 2 and call(E=2048) == 2         # 1 <= E <= 1024
+    assert call(K=0) == 2 and call(K=65) == 2 and call(E=4, K=5) == 2 and call(E=64, K=33) == 2
+    assert call(T=-1) == 2
+    assert call(renorm=2) == 9
+    assert call(T=0) == 0                               # no-op
+    assert f(None, 4, 256, fake, 64, 8, 1, fake, fake, fake, None) == 1
+    assert f(ctypes.c_void_p(0x1004), 4, 256, fake, 64, 8, 1, fake, fake, fake, None) == 3
+
+
 def test_quantize_host_validation(m):
     q = m.lib().nvfp4_quantize
     fake = ctypes.c_void_p(0x1000)
