@@ -167,6 +167,24 @@ def test_routing_edge_cases(gpu, orc):
     _stage_checks(orc, layer1, wl1.x, wl1.ids, wl1.probs, out1, 0)
 
 
+@pytest.mark.parametrize("shape", [
+    W.MoEShape(T=50, H=128, E=1, K=1, I=128),   # one expert; one 128-column K step in both GEMMs;
+                                                # FC2's 128 output columns leave two of four waves idle
+    W.MoEShape(T=37, H=384, E=5, K=5, I=384),   # every token to every expert (K = E); 3 K steps;
+                                                # FC2 N = 384: a half-filled column tile
+    W.MoEShape(T=70, H=640, E=6, K=3, I=256),   # 5 K steps in FC1, 2 in FC2; FC2 N = 640
+])
+def test_unusual_shapes_all_stages(gpu, orc, shape):
+    """Layer shapes away from the workloads: K-step counts of 1, 2, 3, 5; column
+    tiles with idle waves; a single expert; K = E."""
+    m, dev = gpu
+    wl = W.MoEWorkload(f"shape_H{shape.H}_I{shape.I}_E{shape.E}_K{shape.K}", 12, shape)
+    layer = Layer(m, dev, wl, max_tokens=shape.T)
+    out = layer.forward(wl.x, wl.ids, wl.probs)
+    _stage_checks(orc, layer, wl.x, wl.ids, wl.probs, out, 0)
+    assert m.device_error(layer.cfg, layer.ws) == 0
+
+
 def test_zero_tokens_is_noop(gpu):
     import torch
     m, dev = gpu
