@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--tokens", type=int, default=4096)
     ap.add_argument("--cold-steps", type=int, default=10, help="extra forwards timed after a cache-evicting write")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-sized (T = 1, 8, 64) forwards")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -196,6 +197,36 @@ def main():
             cold.append(e0.elapsed_time(e1))
         del scratch
 
+    # Decode-sized forwards (secondary): the first n tokens of the workload, one
+    # forward captured into a HIP graph and replayed back to back, and the same
+    # forward launched eagerly; microseconds per forward.
+    decode = {}
+    if not args.no_decode:
+        for n in (1, 8, 64):
+            xs, ids_s, pr_s = x[:n].contiguous(), ids[:n].contiguous(), probs[:n].contiguous()
+            out_s = torch.empty((n, H), dtype=torch.int16, device=dev)
+            for _ in range(20):
+                m.moe_expert_forward(cfg, xs, ids_s, pr_s, qw, ws, out=out_s)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record(stream)
+            for _ in range(200):
+                m.moe_expert_forward(cfg, xs, ids_s, pr_s, qw, ws, out=out_s, stream=stream)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                m.moe_expert_forward(cfg, xs, ids_s, pr_s, qw, ws, out=out_s)
+            for _ in range(20):
+                g.replay()
+            ev[2].record(stream)
+            for _ in range(200):
+                g.replay()
+            ev[3].record(stream)
+            torch.cuda.synchronize()
+            decode[f"T{n}"] = {"eager_us": ev[0].elapsed_time(ev[1]) / 200 * 1e3,
+                               "graph_us": ev[2].elapsed_time(ev[3]) / 200 * 1e3}
+            del g
+
     P = T * K
     layer_flop = 2.0 * P * 3 * H * I
     fc1_flop = 2.0 * P * H * 2 * I
@@ -240,6 +271,8 @@ def main():
                                 "frac_hbm_peak": wq_bytes / (wq_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                                 "what": "W1 [E,2I,H] and W2 [E,H,I] BF16 read, NVFP4 codes/scales/g written"},
     }
+    if decode:
+        result["decode"] = decode
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, w1, w2, args.cpu_seconds)
     print(json.dumps(result))

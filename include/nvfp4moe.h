@@ -261,10 +261,14 @@ NVFP4MOE_API int nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const nvf
  * tokens from `seed` on the host (a counter-based generator), runs every probe
  * alone, in decode batches of every size 1..max_decode_batch with the probe
  * at a varying position among fillers, and inside one prefill batch of
- * prefill_tokens tokens holding all probes; then compares each probe's output
- * bits with its batch-1 result.  Allocates its own device buffers (it is not
- * a forward-path call) and syncs.  report_host (host, may be NULL) receives
- * {n_compared, n_mismatched_tokens, first_bad_probe, first_bad_batch}.
+ * prefill_tokens tokens holding all probes, and that prefill batch once more
+ * through the masked layout (capacity: the largest expert count rounded up to
+ * 32; article section 4.4, two layouts, same row results); then compares each
+ * probe's output bits with its batch-1 result.  Allocates its own device
+ * buffers (it is not a forward-path call) and syncs.  report_host (host, may
+ * be NULL) receives {n_compared, n_mismatched_tokens, first_bad_probe,
+ * first_bad_batch}, the batch being its token count, negated for the masked
+ * layout.
  * Returns NVFP4_OK when every bit matches, NVFP4_E_MISMATCH otherwise. */
 NVFP4MOE_API int nvfp4moe_selftest_batch_invariance(const nvfp4moe_config* cfg, const nvfp4_qtensor* W1q,
                                        const nvfp4_qtensor* W2q, uint64_t seed, int32_t n_probe,

@@ -7,6 +7,9 @@
 // runs every probe token alone, then inside decode batches of every size
 // 1..max_decode_batch (probes at varying positions among filler tokens), then
 // inside one prefill batch holding all probes, and compares output bits.
+// Section 4.4 ("two layouts, same row results"): the prefill batch also runs
+// through the masked fixed-capacity layout, and its probes must keep their
+// bits there too.
 //
 // Inputs come from a counter-based generator (SplitMix64 of seed and a
 // counter), so the test needs nothing but the quantized weights.
@@ -172,6 +175,35 @@ extern "C" int nvfp4moe_selftest_batch_invariance(const nvfp4moe_config* cfg, co
             fail(st);
         else
             for (int k = 0; k < n_probe; k++) check(slots[k], k, prefill_tokens);
+        // 4. the same batch in the masked layout, capacity = the largest
+        //    expert count rounded up to 32 (reported as batch -T)
+        if (status == NVFP4_OK) {
+            std::vector<int64_t> cnt(E, 0);
+            for (int p = 0; p < prefill_tokens * K; p++) cnt[bid[p]]++;
+            const int64_t mx = *std::max_element(cnt.begin(), cnt.end());
+            const int32_t cap = (int32_t)std::max<int64_t>(32, (mx + 31) / 32 * 32);
+            const size_t mws_bytes = nvfp4moe_workspace_bytes_masked(cfg, cap);
+            void* mws = nullptr;
+            if (mws_bytes == 0)
+                fail(NVFP4_E_SHAPE);
+            else if (hipMalloc(&mws, mws_bytes) != hipSuccess)
+                fail(NVFP4_E_HIP);
+            else {
+                int st2 = nvfp4moe_moe_expert_forward_masked(cfg, cap, (const uint16_t*)dx, prefill_tokens,
+                                                             (const int32_t*)dids, (const float*)dpr, W1q, W2q,
+                                                             (uint16_t*)dout, mws, mws_bytes, s);
+                if (st2 == NVFP4_OK &&
+                    hipMemcpyAsync(bout.data(), dout, (size_t)prefill_tokens * H * 2, hipMemcpyDeviceToHost, s) !=
+                        hipSuccess)
+                    st2 = NVFP4_E_HIP;
+                if (st2 == NVFP4_OK && hipStreamSynchronize(s) != hipSuccess) st2 = NVFP4_E_HIP;
+                if (st2 != NVFP4_OK)
+                    fail(st2);
+                else
+                    for (int k = 0; k < n_probe; k++) check(slots[k], k, -(int64_t)prefill_tokens);
+                (void)hipFree(mws);
+            }
+        }
     }
     (void)hipFree(dx);
     (void)hipFree(dids);

@@ -330,7 +330,7 @@ def test_selftest_entry_point(gpu):
                                           prefill_tokens=2048)
     print("  selftest report", rep)
     assert st == 0 and rep["n_mismatched"] == 0
-    assert rep["n_compared"] == sum(min(b, 4) for b in range(1, 65)) + 32
+    assert rep["n_compared"] == sum(min(b, 4) for b in range(1, 65)) + 2 * 32  # prefill: both layouts
 
 
 def test_weight_reload_in_place(gpu, orc):
