@@ -89,6 +89,8 @@ def _load():
     lib.orc_router_topk.argtypes = [P, I64, I64, I64, ctypes.c_int, P, P]
     lib.orc_moe_forward_deq.restype = None
     lib.orc_moe_forward_deq.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P, P, ctypes.c_int, P, P, P, P, P]
+    lib.orc_moe_forward_w4a16.restype = None
+    lib.orc_moe_forward_w4a16.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P]
     lib.orc_moe_forward.restype = None
     lib.orc_moe_forward.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, ctypes.c_int, P, P, P,
                                     P, P]
@@ -223,6 +225,30 @@ def route(ids: np.ndarray, n_experts: int, m_align: int):
     if P_pad < 0:
         raise ValueError("expert id out of range")
     return off, pair2row, row2pair[:P_pad].copy()
+
+
+def moe_forward_w4a16(x_bf16, ids, probs, weights: DequantWeights, intermediates: bool = False):
+    """The W4A16 variant (article, section 6: NVFP4 W4A16 routed experts): NVFP4
+    weights, BF16 activations not quantized; epilogues multiply by g^w only.
+    Returns out [T,H] BF16 bits, and with ``intermediates`` per-pair h [P,I], y2 [P,H]."""
+    x = _c(x_bf16, np.uint16)
+    ids = _c(ids, np.int32)
+    probs = _c(probs, np.float32)
+    T, H = x.shape
+    K = ids.shape[1]
+    I = weights.I
+    assert H == weights.H
+    if ids.size and (ids.min() < 0 or ids.max() >= weights.E):
+        raise ValueError("expert id out of range")
+    P = T * K
+    out = np.empty((T, H), np.uint16)
+    h = np.empty((P, I), np.uint16) if intermediates else None
+    y2 = np.empty((P, H), np.uint16) if intermediates else None
+    _load().orc_moe_forward_w4a16(_p(x), T, H, I, K, _p(ids), _p(probs), _p(weights.d1), _p(weights.g1),
+                                  _p(weights.d2), _p(weights.g2), _p(out), _p(h), _p(y2))
+    if intermediates:
+        return out, dict(h=h, y2=y2)
+    return out
 
 
 def router_logits(x_bf16: np.ndarray, w_bf16: np.ndarray) -> np.ndarray:

@@ -462,6 +462,59 @@ void orc_moe_forward_deq(const uint16_t* x, int64_t T, int64_t H, int64_t I, int
 
 /* The same layer with the weights given quantized (logical layout): they are
  * dequantized once, then the layer runs as above. */
+/* The W4A16 variant (the article, section 6: NVFP4 W4A16 routed experts):
+ * the same layer with NVFP4 weights and BF16 activations left unquantized,
+ * computed per (token, slot) pair:
+ *   y1 = bf16((x[t] . W1q[e]^T) g^w1)            [2I], FP64 GEMM
+ *   h  = bf16(silu(gate) * up * p)
+ *   y2 = bf16((h . W2q[e]^T) g^w2)               [H]
+ *   out[t] = bf16(FP32 sum over k of y2[t,k])
+ * Weights as for orc_moe_forward_deq; optional per-pair outputs (NULL to
+ * skip): h [P][I], y2 [P][H]. */
+void orc_moe_forward_w4a16(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t K, const int32_t* ids,
+                           const float* probs, const double* w1d, const float* w1g, const double* w2d,
+                           const float* w2g, uint16_t* out, uint16_t* h_out, uint16_t* y2_out) {
+    int64_t P = T * K;
+    uint16_t* y2 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(P * H));
+#pragma omp parallel
+    {
+        double* a = (double*)malloc(sizeof(double) * (size_t)H);
+        double* hd = (double*)malloc(sizeof(double) * (size_t)I);
+        uint16_t* y1 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(2 * I));
+        uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)I);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t p = 0; p < P; p++) {
+            int64_t t = p / K, e = ids[p];
+            for (int64_t k = 0; k < H; k++) a[k] = orc_bf16_to_double(x[t * H + k]);
+            for (int64_t n = 0; n < 2 * I; n++) {
+                int64_t wr = e * 2 * I + n;
+                const double* w = w1d + wr * H;
+                double acc = 0.0;
+                for (int64_t k = 0; k < H; k++) acc += a[k] * w[k];
+                y1[n] = orc_double_to_bf16(acc * (double)w1g[wr]);
+            }
+            float amax2;
+            orc_swiglu_prob(y1, probs + p, 1, I, h, &amax2);
+            for (int64_t k = 0; k < I; k++) hd[k] = orc_bf16_to_double(h[k]);
+            for (int64_t m = 0; m < H; m++) {
+                int64_t wr = e * H + m;
+                const double* w = w2d + wr * I;
+                double acc = 0.0;
+                for (int64_t k = 0; k < I; k++) acc += hd[k] * w[k];
+                y2[p * H + m] = orc_double_to_bf16(acc * (double)w2g[wr]);
+            }
+            if (h_out) memcpy(h_out + p * I, h, sizeof(uint16_t) * (size_t)I);
+        }
+        free(a);
+        free(hd);
+        free(y1);
+        free(h);
+    }
+    orc_combine(y2, T, K, H, out);
+    if (y2_out) memcpy(y2_out, y2, sizeof(uint16_t) * (size_t)(P * H));
+    free(y2);
+}
+
 void orc_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, int64_t K,
                      const int32_t* ids, const float* probs, const uint8_t* w1c, const uint8_t* w1s,
                      const float* w1g, const uint8_t* w2c, const uint8_t* w2s, const float* w2g, int mode,
