@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--tokens", type=int, default=4096)
     ap.add_argument("--cold-steps", type=int, default=10, help="extra forwards timed after a cache-evicting write")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-sized (T = 1, 8, 64) forwards")
+    ap.add_argument("--no-w4a16", action="store_true", help="skip the W4A16 variant's forwards")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -197,6 +198,22 @@ def main():
             cold.append(e0.elapsed_time(e1))
         del scratch
 
+    # The W4A16 variant (secondary): the same workload with BF16 activations.
+    w16 = None
+    if not args.no_w4a16:
+        for _ in range(20):
+            m.moe_expert_forward_w4a16(cfg, x, ids, probs, qw, ws, out=out)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(50):
+            m.moe_expert_forward_w4a16(cfg, x, ids, probs, qw, ws, out=out, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        w16_ms = ev[0].elapsed_time(ev[1]) / 50
+        w16 = {"ms_per_step": w16_ms, "tokens_per_s": T / (w16_ms / 1e3),
+               "tflops": 2.0 * T * K * 3 * H * I / (w16_ms / 1e3) / 1e12,
+               "what": "NVFP4 weights x BF16 activations (bf16 MFMA), same routing, producer and combine"}
+
     # Decode-sized forwards (secondary): the first n tokens of the workload, one
     # forward captured into a HIP graph and replayed back to back, and the same
     # forward launched eagerly; microseconds per forward.
@@ -273,6 +290,8 @@ def main():
     }
     if decode:
         result["decode"] = decode
+    if w16:
+        result["w4a16"] = w16
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, w1, w2, args.cpu_seconds)
     print(json.dumps(result))

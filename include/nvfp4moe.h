@@ -162,6 +162,20 @@ NVFP4MOE_API int nvfp4moe_moe_expert_forward(const nvfp4moe_config* cfg, const u
                                 const float* probs, const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q,
                                 uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The W4A16 variant of the expert forward (the article, section 6: NVFP4
+ * W4A16 routed experts): the same sort, SwiGLU producer, combine, arguments,
+ * workspace and errors as nvfp4moe_moe_expert_forward, with the activations
+ * left in BF16 instead of quantized (x into FC1, h into FC2; cfg->scale_round
+ * is unused), so each epilogue multiplies by g^w only:
+ *   y1 = bf16((x . W1q[e]^T) g^w1), h = bf16(silu(gate) * up * p),
+ *   y2 = bf16((h . W2q[e]^T) g^w2), out[t] = bf16(FP32 slot-order sum of y2).
+ * Per-token results are bitwise independent of the batch, as for the W4A4
+ * forward.  The workspace's quantized-activation buffers are not written. */
+NVFP4MOE_API int nvfp4moe_moe_expert_forward_w4a16(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T,
+                                                   const int32_t* ids, const float* probs, const nvfp4_qtensor* W1q,
+                                                   const nvfp4_qtensor* W2q, uint16_t* out, void* workspace,
+                                                   size_t workspace_bytes, void* stream);
+
 /* The same forward, recording caller-created hipEvent_t events[i] on `stream`
  * at each stage boundary, for timing the stages inside a timed region
  * (events[0] before the sort, [1] after the sort and the quantization of X,

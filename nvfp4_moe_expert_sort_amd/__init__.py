@@ -26,7 +26,7 @@ EXPORTS = ["nvfp4_status_str", "nvfp4_quantize", "nvfp4moe_weight_bytes", "nvfp4
            "nvfp4moe_workspace_bytes", "nvfp4moe_moe_expert_forward", "nvfp4moe_moe_expert_forward_events",
            "nvfp4moe_device_error",
            "nvfp4moe_workspace_layout", "nvfp4moe_workspace_bytes_masked", "nvfp4moe_workspace_layout_masked",
-           "nvfp4moe_moe_expert_forward_masked", "nvfp4moe_router_topk", "nvfp4_linear_workspace_bytes", "nvfp4_linear",
+           "nvfp4moe_moe_expert_forward_masked", "nvfp4moe_moe_expert_forward_w4a16", "nvfp4moe_router_topk", "nvfp4_linear_workspace_bytes", "nvfp4_linear",
            "nvfp4moe_selftest_batch_invariance"]
 
 
@@ -81,6 +81,7 @@ def lib():
         "nvfp4moe_workspace_bytes_masked": (sz, [cfgp, i32]),
         "nvfp4moe_workspace_layout_masked": (ctypes.c_int, [cfgp, i32, ctypes.POINTER(WsLayout)]),
         "nvfp4moe_moe_expert_forward_masked": (ctypes.c_int, [cfgp, i32, vp, i32, vp, vp, qtp, qtp, vp, vp, sz, vp]),
+        "nvfp4moe_moe_expert_forward_w4a16": (ctypes.c_int, [cfgp, vp, i32, vp, vp, qtp, qtp, vp, vp, sz, vp]),
         "nvfp4moe_router_topk": (ctypes.c_int, [vp, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp]),
         "nvfp4_linear_workspace_bytes": (sz, [i64, i64]),
         "nvfp4_linear": (ctypes.c_int, [vp, i64, i64, qtp, vp, i32, vp, sz, vp]),
@@ -212,6 +213,19 @@ def moe_expert_forward_masked(cfg: Config, capacity: int, x, ids, probs, weights
                                                   ctypes.byref(weights.W1q), ctypes.byref(weights.W2q), _ptr(out),
                                                   _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "nvfp4moe_moe_expert_forward_masked")
+    return out
+
+
+def moe_expert_forward_w4a16(cfg: Config, x, ids, probs, weights: QuantWeights, workspace, out=None, stream=None):
+    """nvfp4moe_moe_expert_forward_w4a16: as moe_expert_forward with BF16 activations (NVFP4 weights only)."""
+    import torch
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, cfg.hidden), dtype=x.dtype, device=x.device)
+    st = lib().nvfp4moe_moe_expert_forward_w4a16(ctypes.byref(cfg), _ptr(x), T, _ptr(ids), _ptr(probs),
+                                                 ctypes.byref(weights.W1q), ctypes.byref(weights.W2q), _ptr(out),
+                                                 _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "nvfp4moe_moe_expert_forward_w4a16")
     return out
 
 

@@ -209,7 +209,8 @@ namespace {
 // capacity 0: the contiguous row layout; > 0: the masked layout.
 int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids, const float* probs,
                  const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q, uint16_t* out, void* workspace,
-                 size_t workspace_bytes, void* stream, void* const* events, int32_t capacity = 0) {
+                 size_t workspace_bytes, void* stream, void* const* events, int32_t capacity = 0,
+                 bool w4a16 = false) {
     if (!cfg) return NVFP4_E_NULL;
     if (!cfg_ok(cfg)) return NVFP4_E_SHAPE;
     if (capacity != 0 && !capacity_ok(cfg, capacity)) return NVFP4_E_SHAPE;
@@ -251,11 +252,52 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     const bool ru = cfg->scale_round == NVFP4_SCALE_RU;
 
     if (!mark(0)) return NVFP4_E_HIP;
-    hipError_t e = launch_route(x, ids, probs, T, (int32_t)H, (int32_t)K, (int32_t)E, capacity, ru, rb, L.pub.rows_cap, s);
+    hipError_t e = launch_route(x, ids, probs, T, (int32_t)H, (int32_t)K, (int32_t)E, capacity, ru, rb, L.pub.rows_cap, s,
+                                !w4a16);
     if (e != hipSuccess || !mark(1)) return NVFP4_E_HIP;
 
     // Static bound on row tiles for this T (the device count is <= this).
     const int64_t mt_bound = ((int64_t)T * K + E * (kMAlign - 1)) / kTileRows + E + 1;
+
+    if (w4a16) {
+        // NVFP4 weights x BF16 activations: FC1 reads x's rows through
+        // row2pair, FC2 reads h as FC1 wrote it; no activation quantizer.
+        W16Params g1{};
+        g1.a = x;
+        g1.row2pair = rb.row2pair;
+        g1.top_k = (int32_t)K;
+        g1.b_codes = W1q->codes;
+        g1.b_scales = W1q->scales;
+        g1.b_g = W1q->g;
+        g1.K = (int32_t)H;
+        g1.N = (int32_t)(2 * I);
+        g1.n_tiles_n = col_tiles(I, kGemmSwiGLU);
+        g1.mtiles = rb.mtiles;
+        g1.n_mtiles = rb.n_mtiles;
+        g1.out = (uint16_t*)(ws + L.pub.h);
+        g1.ld_out = I;
+        g1.row_prob = rb.row_prob;
+        g1.inter = (int32_t)I;
+        e = launch_gemm_w4a16(kGemmSwiGLU, g1, mt_bound, s);
+        if (e != hipSuccess || !mark(2) || !mark(3)) return NVFP4_E_HIP;
+        W16Params g2{};
+        g2.a = g1.out;
+        g2.b_codes = W2q->codes;
+        g2.b_scales = W2q->scales;
+        g2.b_g = W2q->g;
+        g2.K = (int32_t)I;
+        g2.N = (int32_t)H;
+        g2.n_tiles_n = col_tiles(H, kGemmPlain);
+        g2.mtiles = rb.mtiles;
+        g2.n_mtiles = rb.n_mtiles;
+        g2.out = (uint16_t*)(ws + L.pub.y2);
+        g2.ld_out = H;
+        e = launch_gemm_w4a16(kGemmPlain, g2, mt_bound, s);
+        if (e != hipSuccess || !mark(4)) return NVFP4_E_HIP;
+        e = launch_combine(g2.out, rb.pair2row, T, (int32_t)H, (int32_t)K, out, s);
+        if (e != hipSuccess || !mark(5)) return NVFP4_E_HIP;
+        return NVFP4_OK;
+    }
 
     GemmParams f1{};
     f1.a_codes = rb.a_codes;
@@ -338,6 +380,12 @@ int nvfp4moe_moe_expert_forward_masked(const nvfp4moe_config* cfg, int32_t capac
                                        size_t workspace_bytes, void* stream) {
     if (cfg && cfg_ok(cfg) && !capacity_ok(cfg, capacity)) return NVFP4_E_SHAPE;
     return forward_impl(cfg, x, T, ids, probs, W1q, W2q, out, workspace, workspace_bytes, stream, nullptr, capacity);
+}
+
+int nvfp4moe_moe_expert_forward_w4a16(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids,
+                                      const float* probs, const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q,
+                                      uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+    return forward_impl(cfg, x, T, ids, probs, W1q, W2q, out, workspace, workspace_bytes, stream, nullptr, 0, true);
 }
 
 int nvfp4moe_device_error(const nvfp4moe_config* cfg, const void* workspace, int32_t* code_host, void* stream) {

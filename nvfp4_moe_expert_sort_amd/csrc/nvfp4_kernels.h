@@ -62,9 +62,31 @@ hipError_t launch_quant_h(const uint16_t* h, int64_t rows_bound, int64_t I, cons
                           bool round_up, hipStream_t stream);
 // capacity 0: contiguous row layout; > 0: masked layout, expert e's rows in
 // the chunk [e * capacity, (e + 1) * capacity) (capacity % kMAlign == 0).
+// quant_x false: X is not quantized and no sorted A1 is built (the W4A16
+// variant reads the BF16 rows of x itself).
 hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* probs, int32_t T, int32_t H, int32_t K,
                         int32_t E, int32_t capacity, bool round_up, const RouteBuffers& rb, int64_t rows_cap,
-                        hipStream_t stream);
+                        hipStream_t stream, bool quant_x = true);
+
+// W4A16 grouped GEMM (NVFP4 weights, BF16 activations): one workgroup per
+// (32-row subtile of a row tile, column tile).
+struct W16Params {
+    const uint16_t* a;         // BF16 activation rows, K columns each
+    const int32_t* row2pair;   // non-null: sorted row r reads row row2pair[r] / top_k of `a` (FC1)
+    int32_t top_k;
+    const uint8_t* b_codes;    // weights, GEMM layout, [E][N][K]
+    const uint8_t* b_scales;
+    const float* b_g;
+    int32_t K, N;
+    int32_t n_tiles_n;         // column tiles (FC1: 128 columns of h; FC2: 256 output columns)
+    const int4* mtiles;
+    const int32_t* n_mtiles;
+    uint16_t* out;
+    int64_t ld_out;
+    const float* row_prob;     // SwiGLU mode: router probability per sorted row
+    int32_t inter;             // SwiGLU mode: I
+};
+hipError_t launch_gemm_w4a16(int mode, const W16Params& P, int64_t mt_bound, hipStream_t stream);
 
 // Router scores logits [T, E] (FP32) and the top-K ids / probabilities per token.
 hipError_t launch_router(const uint16_t* x, int32_t T, int32_t H, const uint16_t* w, int32_t E, int32_t K,

@@ -8,7 +8,9 @@
 // counts, article section 4.6):
 //   route_count   per block of 16 tokens, one wavefront per token: the row
 //                 is read once into registers for its amax and quantization
-//                 (token-major buffer Xq); the block's (t, k) pairs get stable
+//                 (token-major buffer Xq; skipped for BF16 activations, the
+//                 W4A16 variant, which also skips the gather); the block's
+//                 (t, k) pairs get stable
 //                 per-expert ranks in pair order (wave ballots) and a
 //                 per-expert block count; id checks.
 //   route_scan    one block: per-expert exclusive prefix over the blocks,
@@ -42,6 +44,7 @@ constexpr int kCountThreads = kTokPerBlk * 64;  // one wavefront per token of th
 __global__ void __launch_bounds__(kCountThreads) route_count_kernel(const uint16_t* __restrict__ x,
                                                                     const int32_t* __restrict__ ids, int32_t T,
                                                                     int32_t H, int32_t K, int32_t E, int round_up,
+                                                                    int quant_x,
                                                                     int32_t* __restrict__ blk_counts,
                                                                     int32_t* __restrict__ blk_err,
                                                                     int32_t* __restrict__ lrank,
@@ -96,7 +99,7 @@ __global__ void __launch_bounds__(kCountThreads) route_count_kernel(const uint16
     }
     // Each wave quantizes its token's row once (amax in the same pass).
     const int64_t t = t0 + wave;
-    if (t < T) {
+    if (quant_x && t < T) {
         const int64_t groups_per_lane = (H / 32 + kWave - 1) / kWave;
         const uint16_t* xr = x + t * H;
         const bool ru = round_up != 0;
@@ -314,9 +317,10 @@ __global__ void __launch_bounds__(256) route_gather_kernel(int32_t H, int32_t K,
 
 hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* probs, int32_t T, int32_t H, int32_t K,
                         int32_t E, int32_t capacity, bool round_up, const RouteBuffers& rb, int64_t rows_cap,
-                        hipStream_t stream) {
+                        hipStream_t stream, bool quant_x) {
     const int32_t nblk = (T + kTokPerBlk - 1) / kTokPerBlk;
     hipLaunchKernelGGL(route_count_kernel, dim3(nblk), dim3(kCountThreads), 0, stream, x, ids, T, H, K, E, round_up ? 1 : 0,
+                       quant_x ? 1 : 0,
                        rb.blk_counts, rb.blk_err, rb.pair2row /* holds the ranks until route_place */, rb.xq_codes,
                        rb.xq_scales, rb.gx);
     hipError_t st = hipGetLastError();
@@ -330,6 +334,7 @@ hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* prob
                        capacity, rb.blk_counts, rb.expert_off, rb.pair2row, rb.row2pair, rb.row_prob);
     st = hipGetLastError();
     if (st != hipSuccess) return st;
+    if (!quant_x) return hipGetLastError();  // no quantized, sorted copy of X to build
     // Row tiles that can hold rows for this T (the device offsets decide which are used).
     const int64_t rows_bound =
         capacity > 0 ? rows_cap : std::min<int64_t>(rows_cap, (P + (int64_t)E * (kMAlign - 1) + 31) / 32 * 32);
