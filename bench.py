@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--cold-steps", type=int, default=10, help="extra forwards timed after a cache-evicting write")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-sized (T = 1, 8, 64) forwards")
     ap.add_argument("--no-w4a16", action="store_true", help="skip the W4A16 variant's forwards")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense NVFP4 linear")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -198,6 +199,31 @@ def main():
             cold.append(e0.elapsed_time(e1))
         del scratch
 
+    # The dense NVFP4 linear (secondary): X [4096, 2048] with 1 % outliers x50,
+    # W [1536, 2048]; activation quantizer + one GEMM per call.
+    dense = None
+    if not args.no_dense:
+        dw = W.dense(seed=1)
+        xd = torch.from_numpy(dw.x.view(np.int16)).to(dev)
+        wc, wsc, wg = m.quantize(torch.from_numpy(dw.w.view(np.int16)).to(dev), layout=m.LAYOUT_GEMM)
+        Wq = m.qtensor(wc, wsc, wg, 1, dw.N, dw.K)
+        lws = torch.empty((m.linear_workspace_bytes(dw.M, dw.K),), dtype=torch.uint8, device=dev)
+        dout = torch.empty((dw.M, dw.N), dtype=torch.int16, device=dev)
+        for _ in range(20):
+            m.linear(xd, Wq, lws, out=dout)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(100):
+            m.linear(xd, Wq, lws, out=dout, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        d_ms = ev[0].elapsed_time(ev[1]) / 100
+        d_flop = 2.0 * dw.M * dw.N * dw.K
+        dense = {"workload": dw.name, "ms": d_ms, "tflops": d_flop / (d_ms / 1e3) / 1e12,
+                 "frac_f16_mfma_peak": d_flop / (d_ms / 1e3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                 "what": "activation quantizer + one NVFP4 GEMM (f16 MFMA) per call"}
+        del xd, wc, wsc, wg, lws, dout
+
     # The W4A16 variant (secondary): the same workload with BF16 activations.
     w16 = None
     if not args.no_w4a16:
@@ -292,6 +318,8 @@ def main():
         result["decode"] = decode
     if w16:
         result["w4a16"] = w16
+    if dense:
+        result["dense_linear"] = dense
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, w1, w2, args.cpu_seconds)
     print(json.dumps(result))
