@@ -66,6 +66,18 @@ def test_router_parity(gpu, case, renorm):
     print(f"  {case} renorm={renorm}: T={s.T} E={s.E} K={s.K}, max score error {e_l:.3g}, max prob rel {e_p:.3g}")
 
 
+@pytest.mark.parametrize("T,H,E,K", [(33, 144, 50, 7), (5, 2048, 1024, 32), (70, 64, 3, 3)])
+def test_router_ragged_shapes(gpu, T, H, E, K):
+    """Expert counts that are not multiples of 32 or 64, the largest E and K, a
+    token count with a partial 32-token tile, H not a multiple of 64."""
+    m, dev = gpu
+    rng = np.random.default_rng(E)
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    w = _router_weights(E, H, 24)
+    for renorm in (True, False):
+        _check(m, dev, x, w, K, renorm)
+
+
 def test_router_batch_invariance(gpu):
     m, dev = gpu
     wl = W.qwen3(seed=2, T=4096)
