@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-sized (T = 1, 8, 64) forwards")
     ap.add_argument("--no-w4a16", action="store_true", help="skip the W4A16 variant's forwards")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense NVFP4 linear")
+    ap.add_argument("--no-skewed", action="store_true", help="skip the skewed-routing T = 16384 forwards")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -224,6 +225,34 @@ def main():
                  "what": "activation quantizer + one NVFP4 GEMM (f16 MFMA) per call"}
         del xd, wc, wsc, wg, lws, dout
 
+    # Skewed routing (secondary): 16384 tokens whose expert popularity follows
+    # Zipf(1.1) (some experts get 0-8 tokens, the hottest over 2000), on the same
+    # quantized weights; tokens/s of the W4A4 forward.
+    skewed = None
+    if not args.no_skewed:
+        sk = W.skewed(seed=3)
+        ss = sk.shape
+        cfg_s = m.make_config(H, I, E, K, ss.T)
+        ws_s = m.alloc_workspace(cfg_s, dev)
+        xs_ = torch.from_numpy(sk.x.view(np.int16)).to(dev)
+        ids_ = torch.from_numpy(sk.ids).to(dev)
+        pr_ = torch.from_numpy(sk.probs).to(dev)
+        out_ = torch.empty((ss.T, H), dtype=torch.int16, device=dev)
+        for _ in range(10):
+            m.moe_expert_forward(cfg_s, xs_, ids_, pr_, qw, ws_s, out=out_)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(30):
+            m.moe_expert_forward(cfg_s, xs_, ids_, pr_, qw, ws_s, out=out_, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        sk_ms = ev[0].elapsed_time(ev[1]) / 30
+        cnt = sk.expert_counts()
+        skewed = {"workload": sk.name, "tokens": ss.T, "ms_per_step": sk_ms, "tokens_per_s": ss.T / (sk_ms / 1e3),
+                  "tflops": 2.0 * ss.T * K * 3 * H * I / (sk_ms / 1e3) / 1e12,
+                  "expert_rows_min_max": [int(cnt.min()), int(cnt.max())]}
+        del ws_s, xs_, ids_, pr_, out_
+
     # The W4A16 variant (secondary): the same workload with BF16 activations.
     w16 = None
     if not args.no_w4a16:
@@ -320,6 +349,8 @@ def main():
         result["w4a16"] = w16
     if dense:
         result["dense_linear"] = dense
+    if skewed:
+        result["skewed"] = skewed
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, w1, w2, args.cpu_seconds)
     print(json.dumps(result))
