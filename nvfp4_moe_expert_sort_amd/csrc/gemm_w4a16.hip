@@ -5,17 +5,19 @@
 // accumulation in one fixed K order, and the epilogue multiplies by g^w only
 // (the activations carry no outer scale) before the BF16 cast.
 //
-// Design (gfx950): one workgroup per (32-row subtile, column tile); each of
-// its 4 waves owns 2 MFMA column tiles (FC1: 32 gate and the matching 32 up
-// rows of W1; FC2: 64 output columns).  Both operands go straight from memory
-// into registers in the MFMA operand layout: in the GEMM layout lane
-// (h*32 + r) holds weight row r, columns [64c + 32h, 64c + 32h + 32), and the
-// MFMA of k-step j of chunk c takes its columns 8j .. 8j + 7, so the matching
-// BF16 activations are 16 contiguous bytes of row r.  Weights are decoded
-// exactly: E2M1 x E4M3 has at most 6 significant bits, exact in BF16; the
-// products of BF16 values are exact in FP32.  FC1 reads each sorted row's
-// token row of x through row2pair (no sorted copy of x is built).  No LDS,
-// no split-K, no configuration chosen by the token count.
+// Design (gfx950): one workgroup of 4 waves per (row tile of up to 128 rows,
+// column tile); each wave owns 2 MFMA column tiles (FC1: 32 gate and the
+// matching 32 up rows of W1; FC2: 64 output columns) for all the tile's rows.
+// For every 128-column step wave w loads the BF16 rows of 32-row subtile w
+// into LDS in the MFMA operand layout (in the GEMM layout lane (h*32 + r)
+// holds weight row r, columns [64c + 32h, 64c + 32h + 32), and the MFMA of
+// k-step j of chunk c takes its columns 8j .. 8j + 7, so the matching
+// activations are 16 contiguous bytes of row r); every wave reads its A
+// operands there and decodes its own weight columns in registers, exactly:
+// E2M1 x E4M3 has at most 6 significant bits, exact in BF16, and products of
+// BF16 values are exact in FP32.  FC1 reads each sorted row's token row of x
+// through row2pair (no sorted copy of x is built).  No split-K, no
+// configuration chosen by the token count.
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
@@ -52,35 +54,38 @@ __device__ __forceinline__ float w16_silu(float a) {
     return a * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-template <int MODE>
-__global__ void __launch_bounds__(256) gemm_w4a16_kernel(W16Params P) {
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t nt = blockIdx.x % P.n_tiles_n, rest = blockIdx.x / P.n_tiles_n;
-    const int64_t sub = rest % 4, mt = rest / 4;
-    if (mt >= *P.n_mtiles) return;
-    const int4 d = P.mtiles[mt];
-    if (sub >= d.z) return;
-    const int32_t row0 = d.x + 32 * (int32_t)sub, expert = d.y, row_end = d.w;
+// LDS: this step's and the next step's activation fragments,
+// [buffer][32-row subtile][64-column chunk][k-step][lane] x 16 bytes.
+struct W16SharedA {
+    u32x4 a[2][4][2][4][64];
+};
 
+template <int MODE, int NSUB>
+__device__ __forceinline__ void w16_tile(const W16Params& P, W16SharedA& S, int32_t row0, int32_t expert,
+                                         int32_t row_end, int32_t nt) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int32_t bcol[2];
     bool active;
     if (MODE == kGemmSwiGLU) {
-        const int32_t hc = (int32_t)nt * 128 + 32 * wave;
+        const int32_t hc = nt * 128 + 32 * wave;
         active = hc < P.inter;
         bcol[0] = hc;
         bcol[1] = P.inter + hc;
     } else {
-        const int32_t c = (int32_t)nt * 256 + 64 * wave;
+        const int32_t c = nt * 256 + 64 * wave;
         active = c < P.N;
         bcol[0] = c;
         bcol[1] = c + 32;
     }
-    if (!active) return;
-
+    // An idle wave still loads its subtile's activations (the others need
+    // them) and reads wave 0's weight columns, which it never uses.
+    const int32_t wcol = active ? 0 : (MODE == kGemmSwiGLU ? 32 : 64) * wave;
     const int r = lane & 31, h = lane >> 5;
     const int64_t K = P.K, kc64 = K >> 6, kc128 = K >> 7;
-    // this lane's activation row
-    const int64_t arow = row0 + r;
+    // activation row of this wave's subtile (a wave past the tile's subtiles
+    // re-reads subtile 0 and stores nothing)
+    const bool aload = wave < NSUB;
+    const int64_t arow = row0 + 32 * (aload ? wave : 0) + r;
     int64_t src = arow;
     if (P.row2pair) {
         const int32_t pair = P.row2pair[arow];
@@ -91,65 +96,134 @@ __global__ void __launch_bounds__(256) gemm_w4a16_kernel(W16Params P) {
     const uint8_t* bs[2];
 #pragma unroll
     for (int jt = 0; jt < 2; jt++) {
-        const int64_t rt = ((int64_t)expert * P.N + bcol[jt]) >> 5;
+        const int64_t rt = ((int64_t)expert * P.N + bcol[jt] - wcol) >> 5;
         bc[jt] = P.b_codes + rt * kc64 * 1024 + lane * 16;
         bs[jt] = P.b_scales + rt * kc128 * 256 + lane * 4;
     }
-
-    f32x16 acc[2] = {f32x16{}, f32x16{}};
-    for (int64_t cp = 0; cp < kc128; cp++) {  // 128 columns: two 64-column chunks
-        u32x4 av[2][4], bv[2][2];
-        uint32_t sw[2];
+    auto load_a = [&](int64_t cp, int ch, u32x4 (&v)[4]) {
 #pragma unroll
-        for (int ch = 0; ch < 2; ch++) {
-#pragma unroll
-            for (int j = 0; j < 4; j++) av[ch][j] = *reinterpret_cast<const u32x4*>(a + 128 * cp + 64 * ch + 8 * j);
-#pragma unroll
-            for (int jt = 0; jt < 2; jt++) bv[ch][jt] = *reinterpret_cast<const u32x4*>(bc[jt] + (2 * cp + ch) * 1024);
-        }
-#pragma unroll
-        for (int jt = 0; jt < 2; jt++) sw[jt] = *reinterpret_cast<const uint32_t*>(bs[jt] + cp * 256);
+        for (int ks = 0; ks < 4; ks++) v[ks] = *reinterpret_cast<const u32x4*>(a + 128 * cp + 64 * ch + 8 * ks);
+    };
+    auto load_b = [&](int64_t cp, u32x4 (&v)[2][2], uint32_t (&sw)[2]) {
 #pragma unroll
         for (int ch = 0; ch < 2; ch++)
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+            for (int jt = 0; jt < 2; jt++) v[ch][jt] = *reinterpret_cast<const u32x4*>(bc[jt] + (2 * cp + ch) * 1024);
 #pragma unroll
-                for (int jt = 0; jt < 2; jt++) {
-                    // scale byte (ch*2 + j/2) of the dword: the 16-column block of k-step j
-                    const float s = w16_scale(sw[jt], ch * 2 + (j >> 1));
-                    const w16_bf16x8 bw = w16_decode8(bv[ch][jt][j], s);
-                    acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(w16_bf16x8, av[ch][j]), bw,
-                                                                      acc[jt], 0, 0, 0);
-                }
-    }
+        for (int jt = 0; jt < 2; jt++) sw[jt] = *reinterpret_cast<const uint32_t*>(bs[jt] + cp * 256);
+    };
+    auto store_a = [&](int buf, int ch, const u32x4 (&v)[4]) {
+        if (!aload) return;
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) S.a[buf][wave][ch][ks][lane] = v[ks];
+    };
 
-    // Register i of an MFMA tile: row (i/4)*8 + h*4 + i%4, column r.
+    f32x16 acc[NSUB][2];
+#pragma unroll
+    for (int i = 0; i < NSUB; i++) {
+        acc[i][0] = f32x16{};
+        acc[i][1] = f32x16{};
+    }
+    // The next step's activations pass through registers one 64-column chunk
+    // at a time: chunk 0 is loaded at the step's start and stored to LDS
+    // halfway, chunk 1 is loaded then and stored at the step's end.
+    u32x4 av[4], bcur[2][2], bnxt[2][2];
+    uint32_t scur[2], snxt[2];
+    load_a(0, 0, av);
+    load_b(0, bcur, scur);
+    store_a(0, 0, av);
+    load_a(0, 1, av);
+    store_a(0, 1, av);
+    __syncthreads();
+    for (int64_t cp = 0; cp < kc128; cp++) {
+        const int buf = (int)(cp & 1);
+        const int64_t cn = cp + 1 < kc128 ? cp + 1 : cp;  // the last step re-reads its own operands
+        load_a(cn, 0, av);
+        load_b(cn, bnxt, snxt);
+#pragma unroll
+        for (int st = 0; st < 8; st++) {
+            const int ch = st >> 2, ks = st & 3;
+            if (st == 4) {
+                store_a(buf ^ 1, 0, av);
+                load_a(cn, 1, av);
+            }
+            w16_bf16x8 af[NSUB];
+#pragma unroll
+            for (int i = 0; i < NSUB; i++) af[i] = __builtin_bit_cast(w16_bf16x8, S.a[buf][i][ch][ks][lane]);
+            w16_bf16x8 bw[2];
+#pragma unroll
+            for (int jt = 0; jt < 2; jt++) bw[jt] = w16_decode8(bcur[ch][jt][ks], w16_scale(scur[jt], 2 * ch + (ks >> 1)));
+#pragma unroll
+            for (int i = 0; i < NSUB; i++)
+#pragma unroll
+                for (int jt = 0; jt < 2; jt++)
+                    acc[i][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bw[jt], acc[i][jt], 0, 0, 0);
+        }
+        store_a(buf ^ 1, 1, av);  // step cp+1's fragments are in the other buffer
+        __syncthreads();
+#pragma unroll
+        for (int ch = 0; ch < 2; ch++)
+#pragma unroll
+            for (int jt = 0; jt < 2; jt++) bcur[ch][jt] = bnxt[ch][jt];
+        scur[0] = snxt[0];
+        scur[1] = snxt[1];
+    }
+    if (!active) return;
+
+    // Register i of MFMA tile (t, jt): row 32t + (i/4)*8 + h*4 + i%4 of the
+    // tile, column r of column tile jt.  Offsets from this lane's first row.
     const int64_t wrow0 = (int64_t)expert * P.N;
+    const int32_t ld = (int32_t)P.ld_out, lim = row_end - row0 - h * 4;
+    uint16_t* obase = P.out + (int64_t)(row0 + h * 4) * P.ld_out + r;
     if (MODE == kGemmSwiGLU) {
         const float gg = P.b_g[wrow0 + bcol[0] + r], gu = P.b_g[wrow0 + bcol[1] + r];
+        const float* prob = P.row_prob + row0 + h * 4;
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const int32_t row = row0 + (i >> 2) * 8 + h * 4 + (i & 3);
-            if (row >= row_end) continue;
-            const float yg = __uint_as_float(w16_bf16_rne(acc[0][i] * gg) << 16);
-            const float yu = __uint_as_float(w16_bf16_rne(acc[1][i] * gu) << 16);
-            P.out[(int64_t)row * P.ld_out + bcol[0] + r] = (uint16_t)w16_bf16_rne(w16_silu(yg) * yu * P.row_prob[row]);
-        }
+        for (int t = 0; t < NSUB; t++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int32_t rr = 32 * t + (i >> 2) * 8 + (i & 3);
+                if (rr >= lim) continue;
+                const float yg = __uint_as_float(w16_bf16_rne(acc[t][0][i] * gg) << 16);
+                const float yu = __uint_as_float(w16_bf16_rne(acc[t][1][i] * gu) << 16);
+                obase[rr * ld + bcol[0]] = (uint16_t)w16_bf16_rne(w16_silu(yg) * yu * prob[rr]);
+            }
     } else {
 #pragma unroll
         for (int jt = 0; jt < 2; jt++) {
             const float gw = P.b_g[wrow0 + bcol[jt] + r];
 #pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int32_t row = row0 + (i >> 2) * 8 + h * 4 + (i & 3);
-                if (row < row_end) P.out[(int64_t)row * P.ld_out + bcol[jt] + r] = (uint16_t)w16_bf16_rne(acc[jt][i] * gw);
-            }
+            for (int t = 0; t < NSUB; t++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int32_t rr = 32 * t + (i >> 2) * 8 + (i & 3);
+                    if (rr < lim) obase[rr * ld + bcol[jt]] = (uint16_t)w16_bf16_rne(acc[t][jt][i] * gw);
+                }
         }
     }
 }
 
+// One workgroup of 4 waves per (row tile of up to 128 rows, column tile):
+// the activation tile is loaded once per 128-column step (wave w loads
+// subtile w) into LDS, from where every wave reads its MFMA operands; each
+// wave decodes its own weight columns in registers.
+template <int MODE>
+__global__ void __launch_bounds__(256, 2) gemm_w4a16_kernel(W16Params P) {
+    __shared__ W16SharedA S;
+    const int32_t nt = (int32_t)(blockIdx.x % P.n_tiles_n);
+    const int64_t mt = blockIdx.x / P.n_tiles_n;
+    if (mt >= *P.n_mtiles) return;
+    const int4 d = P.mtiles[mt];
+    switch (d.z) {
+        case 4: w16_tile<MODE, 4>(P, S, d.x, d.y, d.w, nt); break;
+        case 3: w16_tile<MODE, 3>(P, S, d.x, d.y, d.w, nt); break;
+        case 2: w16_tile<MODE, 2>(P, S, d.x, d.y, d.w, nt); break;
+        default: w16_tile<MODE, 1>(P, S, d.x, d.y, d.w, nt); break;
+    }
+}
+
 hipError_t launch_gemm_w4a16(int mode, const W16Params& P, int64_t mt_bound, hipStream_t stream) {
-    const int64_t blocks = mt_bound * 4 * P.n_tiles_n;
+    const int64_t blocks = mt_bound * P.n_tiles_n;
     if (blocks <= 0) return hipSuccess;
     if (mode == kGemmSwiGLU)
         hipLaunchKernelGGL(gemm_w4a16_kernel<kGemmSwiGLU>, dim3((unsigned)blocks), dim3(256), 0, stream, P);
