@@ -54,6 +54,11 @@ __device__ __forceinline__ float w16_silu(float a) {
     return a * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Workgroup barrier ordering LDS accesses only: global loads in flight (the
+// next step's weights) stay in flight; the compiler waits for loaded values
+// where they are used.  The memory clobber keeps accesses on their side.
+__device__ __forceinline__ void w16_barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // LDS: this step's and the next step's activation fragments,
 // [buffer][32-row subtile][64-column chunk][k-step][lane] x 16 bytes.
 struct W16SharedA {
@@ -134,7 +139,9 @@ __device__ __forceinline__ void w16_tile(const W16Params& P, W16SharedA& S, int3
     store_a(0, 0, av);
     load_a(0, 1, av);
     store_a(0, 1, av);
-    __syncthreads();
+    w16_barrier_lds();
+    // The K loop's MFMA stream outranks a co-resident workgroup's epilogue.
+    __builtin_amdgcn_s_setprio(2);
     for (int64_t cp = 0; cp < kc128; cp++) {
         const int buf = (int)(cp & 1);
         const int64_t cn = cp + 1 < kc128 ? cp + 1 : cp;  // the last step re-reads its own operands
@@ -160,7 +167,7 @@ __device__ __forceinline__ void w16_tile(const W16Params& P, W16SharedA& S, int3
                     acc[i][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bw[jt], acc[i][jt], 0, 0, 0);
         }
         store_a(buf ^ 1, 1, av);  // step cp+1's fragments are in the other buffer
-        __syncthreads();
+        w16_barrier_lds();
 #pragma unroll
         for (int ch = 0; ch < 2; ch++)
 #pragma unroll
@@ -168,37 +175,65 @@ __device__ __forceinline__ void w16_tile(const W16Params& P, W16SharedA& S, int3
         scur[0] = snxt[0];
         scur[1] = snxt[1];
     }
+    __builtin_amdgcn_s_setprio(0);
     if (!active) return;
 
     // Register i of MFMA tile (t, jt): row 32t + (i/4)*8 + h*4 + i%4 of the
-    // tile, column r of column tile jt.  Offsets from this lane's first row.
+    // tile, column r of column tile jt.  Each 32-row subtile goes through this
+    // wave's own slice of the (now idle) LDS buffer, so a lane stores 16-byte
+    // pieces of one row; the slices are wave-private and one wave's LDS
+    // accesses complete in order.
+    constexpr int kPitch = 72;  // halves per staged row: 64 columns + 8 pad
+    uint16_t* E = reinterpret_cast<uint16_t*>(&S) + wave * (32 * kPitch);
     const int64_t wrow0 = (int64_t)expert * P.N;
-    const int32_t ld = (int32_t)P.ld_out, lim = row_end - row0 - h * 4;
-    uint16_t* obase = P.out + (int64_t)(row0 + h * 4) * P.ld_out + r;
+    const int rowL = h * 4;
     if (MODE == kGemmSwiGLU) {
         const float gg = P.b_g[wrow0 + bcol[0] + r], gu = P.b_g[wrow0 + bcol[1] + r];
-        const float* prob = P.row_prob + row0 + h * 4;
 #pragma unroll
-        for (int t = 0; t < NSUB; t++)
+        for (int t = 0; t < NSUB; t++) {
 #pragma unroll
             for (int i = 0; i < 16; i++) {
-                const int32_t rr = 32 * t + (i >> 2) * 8 + (i & 3);
-                if (rr >= lim) continue;
+                const int rr = (i >> 2) * 8 + rowL + (i & 3);
+                const int32_t row = min(row0 + 32 * t + rr, row_end - 1);  // rows past the end are not stored
                 const float yg = __uint_as_float(w16_bf16_rne(acc[t][0][i] * gg) << 16);
                 const float yu = __uint_as_float(w16_bf16_rne(acc[t][1][i] * gu) << 16);
-                obase[rr * ld + bcol[0]] = (uint16_t)w16_bf16_rne(w16_silu(yg) * yu * prob[rr]);
+                E[rr * kPitch + r] = (uint16_t)w16_bf16_rne(w16_silu(yg) * yu * P.row_prob[row]);
             }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slice is written
+            __builtin_amdgcn_wave_barrier();
+            // lane l: row l % 32, columns 16 (l / 32) .. + 16 of the wave's 32 h columns
+            const int32_t row = row0 + 32 * t + r;
+            if (row < row_end) {
+                const u32x4* src = reinterpret_cast<const u32x4*>(E + r * kPitch + 16 * h);
+                u32x4* dst = reinterpret_cast<u32x4*>(P.out + (int64_t)row * P.ld_out + bcol[0] + 16 * h);
+                dst[0] = src[0];
+                dst[1] = src[1];
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // read before the next pass overwrites the slice
+            __builtin_amdgcn_wave_barrier();
+        }
     } else {
+        const float g0 = P.b_g[wrow0 + bcol[0] + r], g1 = P.b_g[wrow0 + bcol[1] + r];
 #pragma unroll
-        for (int jt = 0; jt < 2; jt++) {
-            const float gw = P.b_g[wrow0 + bcol[jt] + r];
+        for (int t = 0; t < NSUB; t++) {
 #pragma unroll
-            for (int t = 0; t < NSUB; t++)
+            for (int i = 0; i < 16; i++) {
+                const int rr = (i >> 2) * 8 + rowL + (i & 3);
+                E[rr * kPitch + r] = (uint16_t)w16_bf16_rne(acc[t][0][i] * g0);
+                E[rr * kPitch + 32 + r] = (uint16_t)w16_bf16_rne(acc[t][1][i] * g1);
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+            // lane l: row l % 32, columns 32 (l / 32) .. + 32 of the wave's 64
+            const int32_t row = row0 + 32 * t + r;
+            if (row < row_end) {
+                const u32x4* src = reinterpret_cast<const u32x4*>(E + r * kPitch + 32 * h);
+                u32x4* dst = reinterpret_cast<u32x4*>(P.out + (int64_t)row * P.ld_out + bcol[0] + 32 * h);
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int32_t rr = 32 * t + (i >> 2) * 8 + (i & 3);
-                    if (rr < lim) obase[rr * ld + bcol[jt]] = (uint16_t)w16_bf16_rne(acc[t][jt][i] * gw);
-                }
+                for (int q = 0; q < 4; q++) dst[q] = src[q];
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }
