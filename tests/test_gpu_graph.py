@@ -68,3 +68,27 @@ def test_graph_replay_matches_eager(layer, T):
             assert not torch.equal(out, prev), "replay left the previous output in place"
         prev = out.clone()
     print(f"  T={T}: 3 graph replays == eager forward, bit for bit")
+
+
+def test_concurrent_streams_with_separate_workspaces(layer):
+    """Two forwards in flight at once on two streams, each with its own
+    workspace (the library keeps no mutable global state): each equals the
+    same forward run alone."""
+    import torch
+    m, dev, cfg, qw = layer
+    wa, wb = W.qwen3(seed=8, T=2048), W.qwen3(seed=9, T=1500)
+    ins = [(to_dev(w.x, dev), to_dev(w.ids, dev), to_dev(w.probs, dev)) for w in (wa, wb)]
+    ws = [m.alloc_workspace(cfg, dev) for _ in range(2)]
+    ref = []
+    for (x, ids, probs), w in zip(ins, ws):
+        ref.append(m.moe_expert_forward(cfg, x, ids, probs, qw, w))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(r) for r in ref]
+    for rep in range(3):
+        for (x, ids, probs), w, st, o in zip(ins, ws, streams, outs):
+            with torch.cuda.stream(st):
+                m.moe_expert_forward(cfg, x, ids, probs, qw, w, out=o, stream=st)
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o, r), f"repetition {rep}"
