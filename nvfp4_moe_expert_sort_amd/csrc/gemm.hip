@@ -219,8 +219,6 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
         load_a(cpn, na, nsa);
         load_bs(cpn, nsb);
         if (active) {
-            // Eight k-steps of 16 columns; the A operands of step s+1 are read from
-            // LDS while the MFMAs of step s run.
             half2v bsc[2][2][2];  // [chunk][column tile][lo/hi]
 #pragma unroll
             for (int j = 0; j < 2; j++) {
@@ -230,37 +228,42 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
             half8 acur[NSUB];
 #pragma unroll
             for (int i = 0; i < NSUB; i++) acur[i] = S.a[buf][i][0][0][lane];
+            // Eight k-steps of 16 columns; the A operands of k-step s+1 are read
+            // from LDS and its weights decoded while the MFMAs of k-step s run.
+            half8 bv[2];
+#pragma unroll
+            for (int j = 0; j < 2; j++) bv[j] = decode8(ub[0][j][0], bsc[0][j][0]);
 #pragma unroll
             for (int st = 0; st < 8; st++) {
-                const int ch = st >> 2, ks = st & 3;
                 half8 anxt[NSUB];
                 if (st < 7) {
 #pragma unroll
                     for (int i = 0; i < NSUB; i++) anxt[i] = S.a[buf][i][(st + 1) >> 2][(st + 1) & 3][lane];
                 }
-                half8 bv[2];
-#pragma unroll
-                for (int j = 0; j < 2; j++) bv[j] = decode8(ub[ch][j][ks], bsc[ch][j][ks >> 1]);
-                // Keep the reads above ahead of this step's MFMAs (the
-                // scheduler would otherwise sink each read to its first use).
+                // keep the reads above ahead of this k-step's MFMAs (the
+                // scheduler would otherwise sink each read to its first use)
                 __builtin_amdgcn_sched_barrier(0);
+                half8 bn[2];
+                const int sn = st < 7 ? st + 1 : 7, chn = sn >> 2, ksn = sn & 3;
 #pragma unroll
                 for (int i = 0; i < NSUB; i++)
 #pragma unroll
                     for (int j = 0; j < 2; j++)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(acur[i], bv[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 2; j++) bn[j] = decode8(ub[chn][j][ksn], bsc[chn][j][ksn >> 1]);
                 if (st < 7) {
 #pragma unroll
                     for (int i = 0; i < NSUB; i++) acur[i] = anxt[i];
                 }
                 // The next step's activation fragments (loaded at this step's
                 // start, arrived by its second half) are decoded two per
-                // k-step behind the MFMAs of k-steps 4..7, into the other LDS
-                // buffer; the barrier at the step's end orders them before any
-                // reader.  On the last step they re-decode this step's codes
-                // into a buffer nobody reads, and a wave with no activation
-                // tile of its own (wave >= NSUB) decodes its clamped codes into
-                // an LDS slot no MFMA reads: no branch splits the MFMA stream.
+                // k-step on k-steps 4..7, into the other LDS buffer; the
+                // barrier at the step's end orders them before any reader.  On
+                // the last step they re-decode this step's codes into a buffer
+                // nobody reads, and a wave with no activation tile of its own
+                // (wave >= NSUB) decodes its clamped codes into an LDS slot no
+                // MFMA reads: no branch splits the MFMA stream.
                 if (st >= 4) {
                     half2v sl, sh;
                     if ((st - 4) < 2)
@@ -273,6 +276,19 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
                         S.a[buf ^ 1][ai][fch][fks][lane] = decode8(na[fch][fks], fks < 2 ? sl : sh);
                     }
                 }
+                // The decodes (next k-step's weights; on k-steps 4..7 also the
+                // next step's activations) issue in the shadow of this
+                // k-step's MFMAs, four VALU slots after each, instead of in a
+                // burst between two k-steps: a lone wave on its SIMD keeps its
+                // matrix pipe fed.
+#pragma unroll
+                for (int q = 0; q < NSUB * 2; q++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < 2; j++) bv[j] = bn[j];
             }
         } else {
             decode_a(buf ^ 1, na, nsa);
