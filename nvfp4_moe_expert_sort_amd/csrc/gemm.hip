@@ -240,9 +240,6 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
 #pragma unroll
                     for (int i = 0; i < NSUB; i++) anxt[i] = S.a[buf][i][(st + 1) >> 2][(st + 1) & 3][lane];
                 }
-                // keep the reads above ahead of this k-step's MFMAs (the
-                // scheduler would otherwise sink each read to its first use)
-                __builtin_amdgcn_sched_barrier(0);
                 half8 bn[2];
                 const int sn = st < 7 ? st + 1 : 7, chn = sn >> 2, ksn = sn & 3;
 #pragma unroll
@@ -276,15 +273,17 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
                         S.a[buf ^ 1][ai][fch][fks][lane] = decode8(na[fch][fks], fks < 2 ? sl : sh);
                     }
                 }
-                // The decodes (next k-step's weights; on k-steps 4..7 also the
-                // next step's activations) issue in the shadow of this
-                // k-step's MFMAs, four VALU slots after each, instead of in a
+                // The next k-step's A-operand reads and decodes (its weights;
+                // on k-steps 4..7 also the next step's activations) issue in
+                // the shadow of this k-step's MFMAs -- after each MFMA one LDS
+                // read (the first NSUB) and four VALU slots -- instead of in a
                 // burst between two k-steps: a lone wave on its SIMD keeps its
                 // matrix pipe fed.
 #pragma unroll
                 for (int q = 0; q < NSUB * 2; q++) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    if (q < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
