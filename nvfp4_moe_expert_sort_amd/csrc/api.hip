@@ -103,7 +103,8 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_E_HIP; }
 
-// Persistent GEMM grid: two 4-wave workgroups per CU, at most one per tile.
+// Persistent GEMM grid: two 4-wave workgroups per CU, at most one per tile
+// (FC2 and the dense linear; FC1 launches one workgroup per tile).
 int grid_blocks(int64_t tiles_bound) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
@@ -318,7 +319,13 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     f1.amax_part = (float*)(ws + L.pub.amax2_part);
     f1.n_part = (int32_t)(I / 32);
     f1.inter = (int32_t)I;
-    e = launch_gemm(kGemmSwiGLU, f1, grid_blocks(mt_bound * f1.n_tiles_n), s);
+    // FC1: one workgroup per tile (the static bound; workgroups past the
+    // device-side tile count exit at once), so the hardware dispatcher hands
+    // tiles to whichever CU slot frees first.  Measured on the
+    // Qwen3-30B-A3B-shaped layer at T = 4096: 6 us faster than persistent
+    // workgroups walking static ranges; FC2's shorter tiles (K = I) are
+    // faster persistent.
+    e = launch_gemm(kGemmSwiGLU, f1, (int)(mt_bound * f1.n_tiles_n), s);
     if (e != hipSuccess || !mark(2)) return NVFP4_E_HIP;
 
     uint8_t* a2c = ws + L.pub.a2_codes;

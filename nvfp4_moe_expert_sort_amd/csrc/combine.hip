@@ -23,14 +23,28 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
         float acc[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) acc[j] = 0.0f;
-        for (int k = 0; k < K; k++) {
-            const int32_t r = rows[k];
-            if (r < 0) continue;  // only for ids outside the contract (reported by the error word)
-            const u32x4 v = *reinterpret_cast<const u32x4*>(y2 + (int64_t)r * H + c * 8);
+        // All K rows are loaded before the first add (K <= kMaxTopK, in
+        // groups of 8 to bound the registers), so the loads are in flight
+        // together instead of one round trip per slot.  A pair with no row
+        // (ids outside the contract, reported by the error word) reads row 0
+        // and contributes +0: acc starts at +0 and an FP32 sum of that form
+        // is never -0, so adding +0 leaves every bit unchanged.
+        for (int k0 = 0; k0 < K; k0 += 8) {
+            u32x4 v[8];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                acc[2 * j] = acc[2 * j] + bf16_to_f32(v[j] & 0xFFFFu);
-                acc[2 * j + 1] = acc[2 * j + 1] + bf16_to_f32(v[j] >> 16);
+            for (int i = 0; i < 8; i++) {
+                const int32_t r = k0 + i < K ? rows[k0 + i] : -1;
+                v[i] = *reinterpret_cast<const u32x4*>(y2 + (int64_t)max(r, 0) * H + c * 8);
+                if (r < 0) v[i] = u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                if (k0 + i >= K) break;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    acc[2 * j] = acc[2 * j] + bf16_to_f32(v[i][j] & 0xFFFFu);
+                    acc[2 * j + 1] = acc[2 * j + 1] + bf16_to_f32(v[i][j] >> 16);
+                }
             }
         }
         u32x4 o;
