@@ -35,11 +35,13 @@ __device__ __forceinline__ RowScale row_scale(float amax) {
 // Max of |x| over the 8 BF16 values packed in one u32x4, as a BF16 bit
 // pattern: for finite values the bits of |x| order like the values, so the
 // integer max is exact.
+// The two halves of each word are maxed as a pair of 16-bit integers.
+typedef uint16_t u16x2q __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t absmax8_bits(u32x4 v) {
-    uint32_t m = 0u;
+    u16x2q m = __builtin_bit_cast(u16x2q, v[0] & 0x7FFF7FFFu);
 #pragma unroll
-    for (int j = 0; j < 4; j++) m = max(m, max(v[j] & 0x7FFFu, (v[j] >> 16) & 0x7FFFu));
-    return m;
+    for (int j = 1; j < 4; j++) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2q, v[j] & 0x7FFF7FFFu));
+    return max((uint32_t)m[0], (uint32_t)m[1]);
 }
 
 __device__ __forceinline__ float absmax8(u32x4 v) { return bf16_to_f32(absmax8_bits(v)); }
@@ -64,11 +66,27 @@ __device__ __forceinline__ uint32_t fp4_pair(uint32_t old, float q0, float q1) {
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, q0, q1, 1.0f, SEL);
 }
 
-// Signed quotient |x| / sg with x's sign bit (keeps -0), from a BF16 pattern.
-__device__ __forceinline__ float signed_q(uint32_t b, float sg, float y, bool fast) {
-    const float a = __uint_as_float((b & 0x7FFFu) << 16);
-    const float q = fast ? quot(a, sg, y) : a / sg;
-    return __uint_as_float(__float_as_uint(q) | ((b & 0x8000u) << 16));
+// Signed quotient x / sg, from x's BF16 pattern in the high half of a word
+// (low half zero), carrying x's sign bit.  Every step of quot() is odd in x
+// under round-to-nearest, so for x != 0 this is sign(x) * (|x| / sg) bit for
+// bit; the correction step turns a -0 quotient into +0, so the sign bit is
+// put back from x (one bit-field insert).
+template <bool FAST>
+__device__ __forceinline__ float signed_q(uint32_t xw, float sg, float y) {
+    const float x = __uint_as_float(xw);
+    const float q = FAST ? quot(x, sg, y) : x / sg;
+    return __uint_as_float((__float_as_uint(q) & 0x7FFFFFFFu) | (xw & 0x80000000u));
+}
+
+// Eight E2M1 codes (one word) of the eight BF16 values in v.
+template <bool FAST>
+__device__ __forceinline__ uint32_t codes8(u32x4 v, float sg, float y) {
+    uint32_t acc = 0u;
+    acc = fp4_pair<0>(acc, signed_q<FAST>(v[0] << 16, sg, y), signed_q<FAST>(v[0] & 0xFFFF0000u, sg, y));
+    acc = fp4_pair<1>(acc, signed_q<FAST>(v[1] << 16, sg, y), signed_q<FAST>(v[1] & 0xFFFF0000u, sg, y));
+    acc = fp4_pair<2>(acc, signed_q<FAST>(v[2] << 16, sg, y), signed_q<FAST>(v[2] & 0xFFFF0000u, sg, y));
+    acc = fp4_pair<3>(acc, signed_q<FAST>(v[3] << 16, sg, y), signed_q<FAST>(v[3] & 0xFFFF0000u, sg, y));
+    return acc;
 }
 
 // Quantize one 16-element block (two u32x4 of BF16 pairs) -> two code words and the scale byte.
@@ -89,21 +107,18 @@ __device__ __forceinline__ void quant_block16(u32x4 lo, u32x4 hi, const RowScale
         w1 = w[1];
         return;
     }
-    const float y = 1.0f / sg;                      // IEEE division, once per block
-    const bool fast = y < __builtin_huge_valf();   // a reciprocal that overflows (sg < 2^-128) takes the slow path
-    uint32_t w[2];
-#pragma unroll
-    for (int half = 0; half < 2; half++) {
-        const u32x4 v = half ? hi : lo;
-        uint32_t acc = 0u;
-        acc = fp4_pair<0>(acc, signed_q(v[0] & 0xFFFFu, sg, y, fast), signed_q(v[0] >> 16, sg, y, fast));
-        acc = fp4_pair<1>(acc, signed_q(v[1] & 0xFFFFu, sg, y, fast), signed_q(v[1] >> 16, sg, y, fast));
-        acc = fp4_pair<2>(acc, signed_q(v[2] & 0xFFFFu, sg, y, fast), signed_q(v[2] >> 16, sg, y, fast));
-        acc = fp4_pair<3>(acc, signed_q(v[3] & 0xFFFFu, sg, y, fast), signed_q(v[3] >> 16, sg, y, fast));
-        w[half] = acc;
+    const float y = 1.0f / sg;  // IEEE division, once per block
+    // The reciprocal overflows only for sg < 2^-128 (blocks of subnormal
+    // values).  The choice between the reciprocal path and IEEE division is
+    // taken once for the whole wavefront, so no element carries a branch;
+    // both give the IEEE quotient wherever the reciprocal is finite.
+    if (__all(y < __builtin_huge_valf())) {
+        w0 = codes8<true>(lo, sg, y);
+        w1 = codes8<true>(hi, sg, y);
+    } else {
+        w0 = codes8<false>(lo, sg, y);
+        w1 = codes8<false>(hi, sg, y);
     }
-    w0 = w[0];
-    w1 = w[1];
 }
 
 // Quantize 32 consecutive elements (v[0..3]); with only_first, just the first
