@@ -428,7 +428,7 @@ gemm_kernel(GemmParams P) {
     // Each tile's descriptor is loaded one tile ahead, so a tile's first
     // operand loads do not wait for it.
     auto tile_desc = [&](int64_t t) -> int4 {
-        const int64_t mt = t / P.n_tiles_n;
+        const int64_t mt = (uint32_t)t / (uint32_t)P.n_tiles_n;  // tile indices are < 2^31
         if (P.dense_m >= 0) {
             const int32_t row0 = (int32_t)(mt * kTileRows);
             return make_int4(row0, 0, min(4, (P.dense_m - row0 + kMAlign - 1) / kMAlign), P.dense_m);
@@ -439,7 +439,7 @@ gemm_kernel(GemmParams P) {
     if (t >= t_end) return;
     int4 d = tile_desc(t);
     for (; t < t_end; t += per) {
-        const int32_t nt = (int32_t)(t % P.n_tiles_n);
+        const int32_t nt = (int32_t)((uint32_t)t % (uint32_t)P.n_tiles_n);
         const int4 cur = d;
         if (t + per < t_end) d = tile_desc(t + per);
         switch (cur.z) {

@@ -46,21 +46,24 @@ __global__ void __launch_bounds__(256) quant_h_kernel(const uint16_t* __restrict
                                                       int32_t capacity, const int32_t* __restrict__ expert_count,
                                                       const int32_t* __restrict__ row2pair,
                                                       const float* __restrict__ amax2_part, int n_part,
-                                                      int64_t n_units, uint8_t* __restrict__ codes,
+                                                      int64_t n_row_tiles, uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ scales, float* __restrict__ g,
                                                       int round_up) {
+    // Grid: x covers 32-row tiles (four per block, one per wave), y the
+    // column groups of kQuantHSteps 128-column steps.
     const int lane = threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (unit >= n_units) return;
-    const int64_t cps = I / 128, groups = (cps + kQuantHSteps - 1) / kQuantHSteps;
-    const int64_t rt = unit / groups, cp0 = (unit % groups) * kQuantHSteps;
-    if (!row_tile_used(rt, E, capacity, expert_off, expert_count)) return;
+    const int64_t rt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (rt >= n_row_tiles) return;
+    const int64_t cps = I / 128, cp0 = (int64_t)blockIdx.y * kQuantHSteps;
     const int hh = lane >> 5, rl = lane & 31;
     const int64_t row = rt * 32 + rl;
-    const bool valid = row2pair[row] >= 0;  // padding rows are written as zeros
-    // The h loads go out first (padding rows read in-bounds values that are
-    // never used), then the row's partial maxima: n_part = I / 32 floats,
-    // 16-byte aligned since I % 128 == 0.
+    // Every load is issued before the test of whether this row tile holds an
+    // expert's rows (all rows below the launch bound are in-bounds; a tile
+    // past the last expert's rows reads values that are never used), so the
+    // test's own load does not delay them.  The h loads go out first (padding
+    // rows read in-bounds values that are never used), then the row's pair
+    // and partial maxima: n_part = I / 32 floats, 16-byte aligned since
+    // I % 128 == 0.
     u32x4 v[kQuantHSteps][2][4];
 #pragma unroll
     for (int s = 0; s < kQuantHSteps; s++) {
@@ -68,14 +71,24 @@ __global__ void __launch_bounds__(256) quant_h_kernel(const uint16_t* __restrict
 #pragma unroll
         for (int ch = 0; ch < 2; ch++) load32(h + row * I + 64 * (2 * cp + ch) + 32 * hh, false, v[s][ch]);
     }
-    const float4* part = reinterpret_cast<const float4*>(amax2_part + row * n_part);
-    float amax = 0.0f;
-#pragma unroll 8
-    for (int i = 0; i < n_part / 4; i++) {
-        const float4 q = part[i];
-        amax = fmaxf(amax, fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w)));
+    const int32_t pr = row2pair[row];
+    // Row amax: the maxima are non-negative floats, which order like their
+    // bit patterns, so an integer max is exact.  They are read eight 16-byte
+    // vectors at a time, all in flight together (indices past the row's last
+    // vector re-read it).
+    const u32x4* part = reinterpret_cast<const u32x4*>(amax2_part + row * n_part);
+    const int n4 = n_part / 4;
+    uint32_t mbits = 0u;
+    for (int i0 = 0; i0 < n4; i0 += 8) {
+        u32x4 q[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) q[j] = part[min(i0 + j, n4 - 1)];
+#pragma unroll
+        for (int j = 0; j < 8; j++) mbits = max(mbits, max(max(q[j][0], q[j][1]), max(q[j][2], q[j][3])));
     }
-    if (!valid) amax = 0.0f;
+    if (!row_tile_used(rt, E, capacity, expert_off, expert_count)) return;
+    const bool valid = pr >= 0;  // padding rows are written as zeros
+    const float amax = valid ? __uint_as_float(mbits) : 0.0f;
     const RowScale rs = row_scale(amax);
 #pragma unroll
     for (int s = 0; s < kQuantHSteps; s++) {
@@ -109,10 +122,11 @@ hipError_t launch_quant_h(const uint16_t* h, int64_t rows_bound, int64_t I, cons
                           int32_t capacity, const int32_t* expert_count, const int32_t* row2pair,
                           const float* amax2_part, int n_part, uint8_t* codes, uint8_t* scales, float* g,
                           bool round_up, hipStream_t stream) {
-    const int64_t n_units = rows_bound / 32 * ((I / 128 + kQuantHSteps - 1) / kQuantHSteps);
-    if (n_units <= 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_h_kernel, dim3((unsigned)((n_units + 3) / 4)), dim3(256), 0, stream, h, I, expert_off, E,
-                       capacity, expert_count, row2pair, amax2_part, n_part, n_units, codes, scales, g, round_up ? 1 : 0);
+    const int64_t n_row_tiles = rows_bound / 32, groups = (I / 128 + kQuantHSteps - 1) / kQuantHSteps;
+    if (n_row_tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_h_kernel, dim3((unsigned)((n_row_tiles + 3) / 4), (unsigned)groups), dim3(256), 0, stream,
+                       h, I, expert_off, E, capacity, expert_count, row2pair, amax2_part, n_part, n_row_tiles, codes,
+                       scales, g, round_up ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(kCountThreads) route_count_kernel(const uint16
             // A token may not name an expert twice: compare with the token's
             // earlier slots, taken from the lanes that hold them (or memory
             // when the token began in the previous group of 64).
-            const int kk = (int)(p % K);
+            const int kk = (int)((uint32_t)p % (uint32_t)K);  // pair indices are < 2^30
             for (int d = 1; d < K; d++) {
                 const int32_t ed = __shfl(e, max(lane - d, 0), kWave);
                 if (valid && d <= kk) {
@@ -250,7 +250,7 @@ __global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restr
         pair2row[p] = -1;
         return;
     }
-    const int64_t blk = (p / K) / kTokPerBlk;
+    const int64_t blk = ((uint32_t)p / (uint32_t)K) / kTokPerBlk;  // pair indices are < 2^30
     const int32_t local = blk_base[blk * E + e] + pair2row[p];  // rank within the expert
     if (capacity > 0 && local >= capacity) {  // past the expert's chunk (error bit 4)
         pair2row[p] = -1;
@@ -274,18 +274,23 @@ __global__ void __launch_bounds__(256) route_gather_kernel(int32_t H, int32_t K,
                                                            const int32_t* __restrict__ row2pair,
                                                            const uint8_t* __restrict__ xq_codes,
                                                            const uint8_t* __restrict__ xq_scales,
-                                                           const float* __restrict__ gx, int64_t n_units,
+                                                           const float* __restrict__ gx, int64_t n_row_tiles,
                                                            uint8_t* __restrict__ a_codes,
                                                            uint8_t* __restrict__ a_scales, float* __restrict__ a_g) {
+    // Grid: x covers 32-row tiles (four per block, one per wave), y the
+    // column groups of kGatherSteps 128-column steps.
     const int lane = threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (unit >= n_units) return;
-    const int64_t cps = H / 128, groups = (cps + kGatherSteps - 1) / kGatherSteps;
-    const int64_t rt = unit / groups, cp0 = (unit % groups) * kGatherSteps;
-    if (!row_tile_used(rt, E, capacity, expert_off, expert_count)) return;
+    const int64_t rt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (rt >= n_row_tiles) return;
+    const int64_t cps = H / 128, cp0 = (int64_t)blockIdx.y * kGatherSteps;
     const int h = lane >> 5, rl = lane & 31;
     const int64_t row = rt * 32 + rl;
-    const int32_t p = row2pair[row];
+    // The row's pair is loaded together with the test of whether this row
+    // tile holds an expert's rows (every row below the launch bound is
+    // in-bounds), not after it.
+    const int32_t p_raw = row2pair[row];
+    if (!row_tile_used(rt, E, capacity, expert_off, expert_count)) return;
+    const int32_t p = p_raw;
     const int64_t t = p >= 0 ? p / K : 0;
     const uint8_t* cs = xq_codes + t * (H / 2) + h * 16;
     const uint8_t* ss = xq_scales + t * (H / 16) + h * 2;
@@ -338,10 +343,10 @@ hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* prob
     // Row tiles that can hold rows for this T (the device offsets decide which are used).
     const int64_t rows_bound =
         capacity > 0 ? rows_cap : std::min<int64_t>(rows_cap, (P + (int64_t)E * (kMAlign - 1) + 31) / 32 * 32);
-    const int64_t n_units = rows_bound / 32 * ((H / 128 + kGatherSteps - 1) / kGatherSteps);
-    hipLaunchKernelGGL(route_gather_kernel, dim3((unsigned)((n_units + 3) / 4)), dim3(256), 0, stream, H, K,
-                       rb.expert_off, E, capacity, rb.expert_count, rb.row2pair, rb.xq_codes, rb.xq_scales, rb.gx, n_units, rb.a_codes,
-                       rb.a_scales, rb.a_g);
+    const int64_t n_row_tiles = rows_bound / 32, groups = (H / 128 + kGatherSteps - 1) / kGatherSteps;
+    hipLaunchKernelGGL(route_gather_kernel, dim3((unsigned)((n_row_tiles + 3) / 4), (unsigned)groups), dim3(256), 0,
+                       stream, H, K, rb.expert_off, E, capacity, rb.expert_count, rb.row2pair, rb.xq_codes, rb.xq_scales,
+                       rb.gx, n_row_tiles, rb.a_codes, rb.a_scales, rb.a_g);
     return hipGetLastError();
 }
 
