@@ -110,8 +110,8 @@ def cpu_baseline(wl, w1, w2, target_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the expert-parallel sharding across GPUs is described in DESIGN.md, not built)", file=sys.stderr)
+        print(f"bench.py: the expert forward runs on one GPU; --gpus {args.gpus} is not supported "
+              "(expert-parallel sharding across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -6,7 +6,7 @@ arithmetic: it draws random tensors, rounds them to BF16 (input plumbing) and
 routes tokens with a softmax/top-k router that stands in for the upstream
 router the pages place before the expert path.
 
-Recipe (stated again in the design doc):
+Recipe:
   * numpy ``default_rng`` streams spawned from ``SeedSequence(seed)``: one
     child each for X, W1, W2, router logits and extras; W1 and W2 spawn one
     grandchild per expert so any expert's weights can be drawn alone.

@@ -18,7 +18,7 @@
  * agent-driven", section 4.4 (elementwise round-to-nearest, one rounding of
  * SiLU(gate)*up) and section 4.5 (FP32 accumulation in top-k slot order).
  *
- * Numeric contract pinned where the pages are silent (listed in the design doc):
+ * Numeric contract pinned where the pages are silent:
  *   g  = fl32(amax / 2688)            (2688 = 6 * 448)
  *   d  = fl32(6 * g)
  *   v  = fl32(amax_block / d)
