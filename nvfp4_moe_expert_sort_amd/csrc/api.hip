@@ -325,7 +325,8 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     // Qwen3-30B-A3B-shaped layer at T = 4096: 6 us faster than persistent
     // workgroups walking static ranges; FC2's shorter tiles (K = I) are
     // faster persistent.
-    e = launch_gemm(kGemmSwiGLU, f1, (int)(mt_bound * f1.n_tiles_n), s);
+    // (Clamped for extreme shapes: workgroups then walk several tiles each.)
+    e = launch_gemm(kGemmSwiGLU, f1, (int)std::min<int64_t>(mt_bound * f1.n_tiles_n, (int64_t)1 << 30), s);
     if (e != hipSuccess || !mark(2)) return NVFP4_E_HIP;
 
     uint8_t* a2c = ws + L.pub.a2_codes;
