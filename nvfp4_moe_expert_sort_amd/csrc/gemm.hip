@@ -104,7 +104,10 @@ constexpr int kWaitLgkm0 = 0xC07F;
 // compiler from moving memory accesses across it.
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int MODE, int NSUB>
+// ADEC false: this wave has no activation subtile of its own (wave >= NSUB)
+// and is compiled without the K loop's activation decodes; the choice is made
+// once per tile by a wave-uniform branch, so the MFMA stream has no branch.
+template <int MODE, int NSUB, bool ADEC>
 __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, SharedB& SB, int32_t row0, int32_t expert,
                                            int32_t row_end, int32_t nt) {
     // wave index as a scalar, so per-wave conditions are scalar branches
@@ -261,10 +264,9 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
                 // k-step on k-steps 4..7, into the other LDS buffer; the
                 // barrier at the step's end orders them before any reader.  On
                 // the last step they re-decode this step's codes into a buffer
-                // nobody reads, and a wave with no activation tile of its own
-                // (wave >= NSUB) decodes its clamped codes into an LDS slot no
-                // MFMA reads: no branch splits the MFMA stream.
-                if (st >= 4) {
+                // nobody reads.  A wave with no activation tile of its own
+                // (wave >= NSUB) is compiled without them.
+                if (ADEC && st >= 4) {
                     half2v sl, sh;
                     if ((st - 4) < 2)
                         scales_of<0>(nsa, sl, sh);
@@ -442,11 +444,27 @@ gemm_kernel(GemmParams P) {
         const int32_t nt = (int32_t)((uint32_t)t % (uint32_t)P.n_tiles_n);
         const int4 cur = d;
         if (t + per < t_end) d = tile_desc(t + per);
+        const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
         switch (cur.z) {
-            case 4: block_tile<MODE, 4>(P, S, SB, cur.x, cur.y, cur.w, nt); break;
-            case 3: block_tile<MODE, 3>(P, S, SB, cur.x, cur.y, cur.w, nt); break;
-            case 2: block_tile<MODE, 2>(P, S, SB, cur.x, cur.y, cur.w, nt); break;
-            default: block_tile<MODE, 1>(P, S, SB, cur.x, cur.y, cur.w, nt); break;
+            case 4: block_tile<MODE, 4, true>(P, S, SB, cur.x, cur.y, cur.w, nt); break;
+            case 3:
+                if (wv < 3)
+                    block_tile<MODE, 3, true>(P, S, SB, cur.x, cur.y, cur.w, nt);
+                else
+                    block_tile<MODE, 3, false>(P, S, SB, cur.x, cur.y, cur.w, nt);
+                break;
+            case 2:
+                if (wv < 2)
+                    block_tile<MODE, 2, true>(P, S, SB, cur.x, cur.y, cur.w, nt);
+                else
+                    block_tile<MODE, 2, false>(P, S, SB, cur.x, cur.y, cur.w, nt);
+                break;
+            default:
+                if (wv < 1)
+                    block_tile<MODE, 1, true>(P, S, SB, cur.x, cur.y, cur.w, nt);
+                else
+                    block_tile<MODE, 1, false>(P, S, SB, cur.x, cur.y, cur.w, nt);
+                break;
         }
         barrier_lds();  // the next tile's prologue overwrites LDS buffer 0
     }
