@@ -262,12 +262,18 @@ __global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restr
     row_prob[row] = probs[p];
 }
 
-constexpr int kGatherSteps = 2;  // 128-column steps per gather wave
+constexpr int kGatherSteps = 2;  // 128-column steps per gather wave (one 128-byte line of a row's codes)
 
-// One wave per (32-row tile, up to kGatherSteps 128-column steps) of the
-// sorted buffer: lane (h*32 + r) copies row r's columns [64c + 32h, +32) of
-// each chunk c from its token's quantized row, so every chunk is written as
-// one contiguous 1 KiB; all loads are issued before the stores.
+// One wave per (32-row tile, two 128-column steps) of the sorted buffer.
+// Codes: the two steps' codes of a row are 128 contiguous bytes of its
+// token's quantized row, so eight lanes read one row's line (lane l: row
+// 8j + l/8, bytes 16 (l % 8)) and each lane stores its 16 bytes straight into
+// its GEMM-layout slot -- for a fixed chunk and half, eight consecutive rows
+// are 128 contiguous bytes there, so stores are whole lines too.  Scales:
+// lane (h, r) reads row r's 8 scale bytes of each step and keeps its GEMM
+// word (bytes 2h, 2h+1, 4+2h, 5+2h).  Padding rows are written as zeros;
+// every load is in bounds (padding rows read token 0, a step past the end
+// re-reads the last one).
 __global__ void __launch_bounds__(256) route_gather_kernel(int32_t H, int32_t K, const int32_t* __restrict__ expert_off,
                                                            int32_t E, int32_t capacity,
                                                            const int32_t* __restrict__ expert_count,
@@ -278,46 +284,48 @@ __global__ void __launch_bounds__(256) route_gather_kernel(int32_t H, int32_t K,
                                                            uint8_t* __restrict__ a_codes,
                                                            uint8_t* __restrict__ a_scales, float* __restrict__ a_g) {
     // Grid: x covers 32-row tiles (four per block, one per wave), y the
-    // column groups of kGatherSteps 128-column steps.
+    // pairs of 128-column steps.
     const int lane = threadIdx.x & 63;
     const int64_t rt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (rt >= n_row_tiles) return;
     const int64_t cps = H / 128, cp0 = (int64_t)blockIdx.y * kGatherSteps;
-    const int h = lane >> 5, rl = lane & 31;
-    const int64_t row = rt * 32 + rl;
-    // The row's pair is loaded together with the test of whether this row
-    // tile holds an expert's rows (every row below the launch bound is
-    // in-bounds), not after it.
-    const int32_t p_raw = row2pair[row];
+    const int q = lane & 7, step = q >> 2, ch = (q >> 1) & 1, hq = q & 1;  // this lane's 16-byte piece
+    const int hs = lane >> 5, rs = lane & 31;                              // this lane's scale word
+    int32_t pc[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) pc[j] = row2pair[rt * 32 + 8 * j + (lane >> 3)];
+    const int32_t ps = row2pair[rt * 32 + rs];
     if (!row_tile_used(rt, E, capacity, expert_off, expert_count)) return;
-    const int32_t p = p_raw;
-    const int64_t t = p >= 0 ? p / K : 0;
-    const uint8_t* cs = xq_codes + t * (H / 2) + h * 16;
-    const uint8_t* ss = xq_scales + t * (H / 16) + h * 2;
-    u32x4 c[kGatherSteps][2];
-    uint32_t sc[kGatherSteps];
+    const int64_t cpq = min(cp0 + step, cps - 1);
+    u32x4 c[4];
 #pragma unroll
-    for (int i = 0; i < kGatherSteps; i++) {
-        const int64_t cp = cp0 + i;
-        c[i][0] = c[i][1] = u32x4{0u, 0u, 0u, 0u};
-        sc[i] = 0u;
-        if (p >= 0 && cp < cps) {
-            c[i][0] = *reinterpret_cast<const u32x4*>(cs + cp * 64);
-            c[i][1] = *reinterpret_cast<const u32x4*>(cs + cp * 64 + 32);
-            sc[i] = (uint32_t)*reinterpret_cast<const uint16_t*>(ss + cp * 8) |
-                    ((uint32_t)*reinterpret_cast<const uint16_t*>(ss + cp * 8 + 4) << 16);
+    for (int j = 0; j < 4; j++) {
+        const int64_t t = pc[j] >= 0 ? (uint32_t)pc[j] / (uint32_t)K : 0;
+        c[j] = *reinterpret_cast<const u32x4*>(xq_codes + t * (H / 2) + cpq * 64 + ch * 32 + hq * 16);
+    }
+    const int64_t ts = ps >= 0 ? (uint32_t)ps / (uint32_t)K : 0;
+    const uint8_t* ss = xq_scales + ts * (H / 16);
+    const u32x2 w0 = *reinterpret_cast<const u32x2*>(ss + min(cp0, cps - 1) * 8);
+    const u32x2 w1 = *reinterpret_cast<const u32x2*>(ss + min(cp0 + 1, cps - 1) * 8);
+    const float gt = gx[ts];
+    const uint32_t sel = hs ? 0x07060302u : 0x05040100u;
+    if (cp0 + step < cps) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int r = 8 * j + (lane >> 3);
+            const u32x4 v = pc[j] >= 0 ? c[j] : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(a_codes + (rt * (H / 64) + 2 * (cp0 + step) + ch) * 1024 + (hq * 32 + r) * 16) = v;
         }
     }
 #pragma unroll
-    for (int i = 0; i < kGatherSteps; i++) {
-        const int64_t cp = cp0 + i;
-        if (cp < cps) {
-            *reinterpret_cast<u32x4*>(a_codes + (rt * (H / 64) + 2 * cp) * 1024 + lane * 16) = c[i][0];
-            *reinterpret_cast<u32x4*>(a_codes + (rt * (H / 64) + 2 * cp + 1) * 1024 + lane * 16) = c[i][1];
-            *reinterpret_cast<uint32_t*>(a_scales + (rt * (H / 128) + cp) * 256 + lane * 4) = sc[i];
+    for (int st = 0; st < kGatherSteps; st++) {
+        if (cp0 + st < cps) {
+            const u32x2 w = st ? w1 : w0;
+            const uint32_t word = ps >= 0 ? __builtin_amdgcn_perm(w[1], w[0], sel) : 0u;
+            *reinterpret_cast<uint32_t*>(a_scales + (rt * (H / 128) + cp0 + st) * 256 + lane * 4) = word;
         }
     }
-    if (cp0 == 0 && h == 0) a_g[row] = p >= 0 ? gx[t] : 0.0f;
+    if (cp0 == 0 && hs == 0) a_g[rt * 32 + rs] = ps >= 0 ? gt : 0.0f;
 }
 
 hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* probs, int32_t T, int32_t H, int32_t K,
