@@ -33,26 +33,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 // E4M3FN byte of a non-negative block scale v.  round_up: the smallest E4M3FN
 // value >= v; otherwise nearest with ties to an even mantissa.  Clamped to
-// 448 (0x7E); 0 for v <= 0.
+// 448 (0x7E); 0 for v <= 0.  The hardware conversion v_cvt_pk_fp8_f32 rounds
+// to nearest even (subnormal codes included); round-up takes the next code
+// when that value lies below v (codes of non-negative values are monotone).
+// Checked on the GPU against an integer encoder written from the format
+// (exponent, 3-bit mantissa, ceil/rint) for every non-negative binary32
+// pattern below 512, both modes: no difference.
 __device__ __forceinline__ uint32_t e4m3_encode(float v, bool round_up) {
     if (!(v > 0.0f)) return 0u;
-    if (v >= 448.0f) return 0x7Eu;
-    if (v < 0.015625f) {                       // below 2^-6: subnormal codes m * 2^-9, m = 0..8
-        float t = v * 512.0f;                  // exact power-of-two scaling
-        float m = round_up ? ceilf(t) : rintf(t);
-        return (uint32_t)m;                    // m == 8 is 2^-6, whose byte is 0x08
-    }
-    uint32_t u = __float_as_uint(v);
-    int e = (int)(u >> 23) - 127;              // -6 .. 8
-    float t = __uint_as_float((u & 0x007FFFFFu) | (130u << 23));  // 8 * 1.mantissa, in [8, 16)
-    float m = round_up ? ceilf(t) : rintf(t);  // 8 .. 16
-    uint32_t mi = (uint32_t)m;
-    if (mi == 16u) {
-        mi = 8u;
-        e += 1;
-    }
-    if (e > 8 || (e == 8 && mi > 14u)) return 0x7Eu;
-    return ((uint32_t)(e + 7) << 3) | (mi - 8u);
+    const float c = fminf(v, 448.0f);
+    uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+    if (round_up && __builtin_amdgcn_cvt_f32_fp8(code, 0) < c) code += 1u;
+    return code;
 }
 
 // E4M3FN byte -> float (gfx950 converts the OCP E4M3FN format in hardware).
