@@ -104,7 +104,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_E_HIP; }
 
 // Persistent GEMM grid: two 4-wave workgroups per CU, at most one per tile
-// (FC2 and the dense linear; FC1 launches one workgroup per tile).
+// (FC2 and the dense linear; FC1 uses the hybrid grid below).
 int grid_blocks(int64_t tiles_bound) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
@@ -112,6 +112,15 @@ int grid_blocks(int64_t tiles_bound) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
     return (int)std::max<int64_t>(8, std::min<int64_t>(tiles_bound, 2 * (int64_t)cus));
+}
+
+// Hybrid GEMM grid (gemm_kernel with persist > 0): `persist` = two
+// workgroups per CU walking a static bulk, then enough one-tile workgroups for
+// the one to two rounds left over (tiles_bound bounds the tail).
+int hybrid_persist() { return std::max(8, grid_blocks(1 << 30) / 8 * 8); }
+int hybrid_grid(int64_t tiles_bound) {
+    const int64_t np = hybrid_persist();
+    return (int)(np + std::min<int64_t>(2 * np + 8, tiles_bound));
 }
 
 int32_t col_tiles(int64_t n, int mode) {
@@ -319,14 +328,15 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     f1.amax_part = (float*)(ws + L.pub.amax2_part);
     f1.n_part = (int32_t)(I / 32);
     f1.inter = (int32_t)I;
-    // FC1: one workgroup per tile (the static bound; workgroups past the
-    // device-side tile count exit at once), so the hardware dispatcher hands
-    // tiles to whichever CU slot frees first.  Measured on the
-    // Qwen3-30B-A3B-shaped layer at T = 4096: 6 us faster than persistent
-    // workgroups walking static ranges; FC2's shorter tiles (K = I) are
-    // faster persistent.
-    // (Clamped for extreme shapes: workgroups then walk several tiles each.)
-    e = launch_gemm(kGemmSwiGLU, f1, (int)std::min<int64_t>(mt_bound * f1.n_tiles_n, (int64_t)1 << 30), s);
+    // FC1: hybrid grid -- two workgroups per CU walk a static bulk of equal
+    // tile counts, and the last one to two rounds of tiles go one per
+    // workgroup to the rest of the grid, which the hardware dispatcher hands
+    // to whichever CU slot frees first.  Measured on the Qwen3-30B-A3B-shaped
+    // layer at T = 4096: about 8 us faster than persistent workgroups alone
+    // and 2-3 us faster than one workgroup per tile; FC2's shorter tiles
+    // (K = I) are fastest persistent.
+    f1.persist = hybrid_persist();
+    e = launch_gemm(kGemmSwiGLU, f1, hybrid_grid(mt_bound * f1.n_tiles_n), s);
     if (e != hipSuccess || !mark(2)) return NVFP4_E_HIP;
 
     uint8_t* a2c = ws + L.pub.a2_codes;

@@ -425,8 +425,27 @@ gemm_kernel(GemmParams P) {
     const int64_t n_mt = P.dense_m >= 0 ? (P.dense_m + kTileRows - 1) / kTileRows : *P.n_mtiles;
     const int64_t total = n_mt * P.n_tiles_n;
     const int64_t nb = gridDim.x;  // a multiple of 8
-    const int64_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = nb >> 3;
-    const int64_t t_begin = total * xcd / 8, t_end = total * (xcd + 1) / 8;
+    const int64_t xcd = blockIdx.x & 7;
+    int64_t slot = blockIdx.x >> 3, per = nb >> 3;
+    int64_t t_begin = total * xcd / 8, t_end = total * (xcd + 1) / 8;
+    if (P.persist > 0) {
+        // Hybrid grid: workgroups [0, persist) walk a static bulk of
+        // (tiles / persist - 1) rounds, exactly that many tiles each; the
+        // remaining one to two rounds go one tile per workgroup to the rest of
+        // the grid, which the dispatcher starts as the persistent ones finish.
+        const int64_t np = P.persist;
+        const int64_t S = (total / np > 1 ? total / np - 1 : 0) * np;
+        if (blockIdx.x < np) {
+            t_begin = S * xcd / 8;
+            t_end = S * (xcd + 1) / 8;
+            per = np >> 3;
+        } else {
+            t_begin = S + (total - S) * xcd / 8;
+            t_end = S + (total - S) * (xcd + 1) / 8;
+            slot = (blockIdx.x - np) >> 3;
+            per = (nb - np) >> 3;
+        }
+    }
     // Each tile's descriptor is loaded one tile ahead, so a tile's first
     // operand loads do not wait for it.
     auto tile_desc = [&](int64_t t) -> int4 {
@@ -438,7 +457,7 @@ gemm_kernel(GemmParams P) {
         return P.mtiles[mt];
     };
     int64_t t = t_begin + slot;
-    if (t >= t_end) return;
+    if (t >= t_end || per <= 0) return;
     int4 d = tile_desc(t);
     for (; t < t_end; t += per) {
         const int32_t nt = (int32_t)((uint32_t)t % (uint32_t)P.n_tiles_n);

@@ -27,6 +27,7 @@ struct GemmParams {
     const int4* mtiles;        // row tiles {row0, expert, 32-row subtiles, end of valid rows}
     const int32_t* n_mtiles;   // device count of row tiles
     int32_t dense_m;           // >= 0: one matrix with this many rows; row tiles implied
+    int32_t persist;           // > 0 (a multiple of 8): hybrid grid, see gemm_kernel
     uint16_t* out;
     int64_t ld_out;
     const float* row_prob;     // SwiGLU mode: router probability per row
