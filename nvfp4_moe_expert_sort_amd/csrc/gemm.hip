@@ -37,9 +37,10 @@
 //    sync).  Workgroups with blockIdx % 8 == x (one XCD under round-robin
 //    dispatch) take one contiguous range of tiles, so an expert's weight slab
 //    and its row tiles meet in that XCD's L2.  The grid is either persistent
-//    (two workgroups per CU, each walking its share of the range) or one
-//    workgroup per tile of a static bound (the hardware dispatcher then
-//    balances the tiles over the CU slots as they free up).
+//    (two workgroups per CU, each walking its share of the range) or hybrid:
+//    persistent workgroups walk a static bulk of equal tile counts and one
+//    workgroup per tile takes the last rounds (the hardware dispatcher then
+//    balances those tiles over the CU slots as they free up).
 //  * No split-K, one K order, one instruction sequence per row for every batch
 //    size: a row's bits depend only on its own inputs.
 #include "nvfp4_device.h"
