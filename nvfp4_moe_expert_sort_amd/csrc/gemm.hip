@@ -387,7 +387,10 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
     } else {
         constexpr int kPitch = 72;  // halves per staged row: 64 columns + 8 pad (144 B, conflict-free)
         uint16_t* E = reinterpret_cast<uint16_t*>(&S) + wave * (32 * kPitch);
-        // one 32-row MFMA tile per pass; lane l then stores half (l/32) of row l%32
+        // one 32-row MFMA tile per pass; the wave's 64 columns of a row are 128
+        // contiguous bytes of the output, so eight lanes store one row (lane l:
+        // row 8q + l/8 of the pass, bytes 16 (l % 8)) and each store
+        // instruction writes eight whole 128-byte lines
 #pragma unroll
         for (int i = 0; i < NSUB; i++) {
 #pragma unroll
@@ -404,13 +407,13 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
             }
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
             __builtin_amdgcn_wave_barrier();
-            const int32_t row = row0 + 32 * i + colL;
-            const int hseg = lane >> 5;
-            if (row < row_end) {
-                const u32x4* src = reinterpret_cast<const u32x4*>(E + colL * kPitch + 32 * hseg);
-                u32x4* dst = reinterpret_cast<u32x4*>(P.out + (int64_t)row * P.ld_out + bcol0[0] + 32 * hseg);
 #pragma unroll
-                for (int q = 0; q < 4; q++) dst[q] = src[q];
+            for (int q = 0; q < 4; q++) {
+                const int r = 8 * q + (lane >> 3), pc = 8 * (lane & 7);
+                const int32_t row = row0 + 32 * i + r;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(E + r * kPitch + pc);
+                if (row < row_end)
+                    *reinterpret_cast<u32x4*>(P.out + (int64_t)row * P.ld_out + bcol0[0] + pc) = v;
             }
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // slice read before the next pass overwrites it
             __builtin_amdgcn_wave_barrier();
