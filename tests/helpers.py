@@ -54,3 +54,63 @@ def rel_l2(got_bits: np.ndarray, ref_bits: np.ndarray):
 
 def bf16(a) -> np.ndarray:
     return W.f32_to_bf16_bits(np.asarray(a, np.float32))
+
+
+def e4m3fn_value(code: int) -> float:
+    """E4M3FN value of a positive code (1..126), from the format: bias 7,
+    three mantissa bits, subnormals m * 2^-9."""
+    e, mant = code >> 3, code & 7
+    return mant * 2.0 ** -9 if e == 0 else 2.0 ** (e - 7) * (1.0 + mant / 8.0)
+
+
+def bf16_exact_bits(v: float) -> int:
+    b = int(W.f32_to_bf16_bits(np.array([v], np.float32))[0])
+    assert W.bf16_bits_to_f32(np.array([b], np.uint16))[0] == np.float32(v), v  # exactly representable
+    return b
+
+
+def scale_tie_targets():
+    """(BF16 bits of a block maximum, expected RU scale code, expected RNE scale code).
+
+    With the row maximum 448, fl32(6 * fl32(448 / 2688)) is exactly 1.0, so a
+    block's scale input v = amax_b / (6 g) equals its maximum: every E4M3FN
+    value, every midpoint between neighbours (ties: RU takes the upper code,
+    RNE the one with the even mantissa, i.e. the even code) and the BF16
+    values either side of each midpoint land on the encoder's decisions."""
+    out = []
+    for c in range(1, 127):
+        out.append((bf16_exact_bits(e4m3fn_value(c)), c, c))
+    lo_mid = bf16_exact_bits(2.0 ** -10)  # between 0 and the smallest subnormal 2^-9
+    out += [(lo_mid, 1, 0), (lo_mid - 1, 1, 0), (lo_mid + 1, 1, 1)]
+    for c in range(1, 126):
+        mid = bf16_exact_bits((e4m3fn_value(c) + e4m3fn_value(c + 1)) / 2)
+        even = c if c % 2 == 0 else c + 1
+        out += [(mid, c + 1, even), (mid - 1, c + 1, c), (mid + 1, c + 1, c + 1)]
+    return out
+
+
+
+def scale_tie_rows(rows_multiple: int = 1):
+    """BF16 rows of 128 columns holding every scale_tie_targets() block maximum:
+    block 0 of each row pins the row maximum at 448 (so 6 g = 1 exactly),
+    blocks 1..7 take one target each; the block's other elements are fixed
+    fractions of its maximum.  Returns (rows, {mode: expected scale codes})."""
+    targets = scale_tie_targets()
+    pattern = np.array([1, -0.75, 0.5, 0.3, -0.2, 0.1, 0.05, -0.9, 0.6, 0.4, -0.33, 0.25, 0.125, -0.01, 0.7, 0.0])
+    per_row = 7
+    n_rows = (len(targets) + per_row - 1) // per_row
+    n_rows = (n_rows + rows_multiple - 1) // rows_multiple * rows_multiple
+    x = np.zeros((n_rows, 128), np.uint16)
+    want = {0: np.zeros((n_rows, 8), np.uint8), 1: np.zeros((n_rows, 8), np.uint8)}
+    for r in range(n_rows):
+        x[r, :16] = W.f32_to_bf16_bits((448.0 * pattern).astype(np.float32))
+        want[0][r, 0] = want[1][r, 0] = 0x7E
+    for i, (bits, ru, rne) in enumerate(targets):
+        r, b = divmod(i, per_row)
+        t = float(W.bf16_bits_to_f32(np.array([bits], np.uint16))[0])
+        blk = W.f32_to_bf16_bits((t * pattern).astype(np.float32))
+        blk[0] = bits  # the block maximum is exactly the target
+        assert np.all((blk & 0x7FFF) <= bits)
+        x[r, 16 * (b + 1):16 * (b + 2)] = blk
+        want[0][r, b + 1], want[1][r, b + 1] = ru, rne
+    return x, want  # blocks without a target stay zero (scale 0)

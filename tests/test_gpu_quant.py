@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import moe_workloads as W
-from tests.helpers import gemm_to_logical, to_dev, to_host
+from tests.helpers import gemm_to_logical, scale_tie_rows, scale_tie_targets, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -146,3 +146,19 @@ def test_quantize_weights_qwen3_experts(gpu, orc):
     _assert_same((c1, s1, to_host(qw.w1_g)), orc.quantize(w1.reshape(-1, s.H), 0), "W1 qwen3")
     c2, s2 = gemm_to_logical(to_host(qw.w2_codes), to_host(qw.w2_scales), s.E * s.H, s.I)
     _assert_same((c2, s2, to_host(qw.w2_g)), orc.quantize(w2.reshape(-1, s.I), 0), "W2 qwen3")
+
+
+def test_scale_encoder_ties(gpu, orc):
+    """The E4M3 block-scale encoder at every decision point, both roundings and
+    layouts: scales equal the format's expectation, codes, scales and g equal
+    the oracle bit for bit."""
+    m, dev = gpu
+    x, want = scale_tie_rows(rows_multiple=32)  # whole 32-row tiles for the GEMM layout
+    for mode in (0, 1):
+        ref = orc.quantize(x, mode)
+        assert np.array_equal(ref[1], want[mode]), f"oracle scales vs the format, mode {mode}"
+        for layout in (m.LAYOUT_LOGICAL, m.LAYOUT_GEMM):
+            got = _gpu_quant(m, dev, x, mode, layout)
+            assert np.array_equal(got[1], want[mode]), f"GPU scales vs the format, mode {mode} layout {layout}"
+            _assert_same(got, ref, f"scale ties mode={mode} layout={layout}")
+    print(f"  {len(scale_tie_targets())} block maxima at the E4M3 decision points, both roundings, both layouts")

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 from tests.exact import frac_to_bf16_bits
+from tests.helpers import scale_tie_rows
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "nvfp4_hand_cases.json")
 
@@ -105,6 +106,21 @@ def test_e4m3_round_up_and_rne(orc):
         assert orc.e4m3_encode(v, 0) == 0x7E and orc.e4m3_encode(v, 1) == 0x7E
     assert orc.e4m3_encode(1e-6, 0) == 0x01 and orc.e4m3_encode(1e-6, 1) == 0x00
     assert orc.e4m3_encode(0.0, 0) == 0 and orc.e4m3_encode(0.0, 1) == 0
+
+
+def test_quantizer_scale_decisions_through_rows(orc):
+    """The whole row path (amax, g, 6 g, v, encoder) at every E4M3 decision
+    point: with a row maximum of 448, 6 g is exactly 1, so each block's scale
+    input is its BF16 maximum; the expected codes follow from the format alone
+    (exact values keep their code; at a midpoint RU takes the upper code and
+    RNE the even one; a BF16 step either side decides by nearest)."""
+    x, want = scale_tie_rows()
+    g = np.float32(448) / np.float32(2688)
+    assert np.float32(6) * g == np.float32(1)
+    for mode in (0, 1):
+        _, sc, gg = orc.quantize(x, mode)
+        assert np.array_equal(sc, want[mode]), f"mode {mode}: {np.argwhere(sc != want[mode])[:5].tolist()}"
+        assert np.all(gg == g)
 
 
 # --- Q: hand cases -----------------------------------------------------------------------------------
