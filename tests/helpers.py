@@ -114,3 +114,55 @@ def scale_tie_rows(rows_multiple: int = 1):
         x[r, 16 * (b + 1):16 * (b + 2)] = blk
         want[0][r, b + 1], want[1][r, b + 1] = ru, rne
     return x, want  # blocks without a target stay zero (scale 0)
+
+
+# E2M1 decision thresholds (midpoints between neighbouring magnitudes) and the
+# code each tie rounds to (the even code), with the codes on either side.
+E2M1_TIES = ((0.25, 0, 0, 1), (0.75, 2, 1, 2), (1.25, 2, 2, 3), (1.75, 4, 3, 4), (2.5, 4, 4, 5), (3.5, 6, 5, 6),
+             (5.0, 6, 6, 7))
+
+
+def code_tie_rows():
+    """BF16 rows of 128 columns and their expected E2M1 codes (both scale
+    roundings give the same here).  Block 0 of each row holds the row maximum
+    2688, so g = 1 exactly; every other block has maximum 6 S for an E4M3FN
+    value S, so its scale is exactly S, and its remaining elements are
+    theta * S for each E2M1 decision threshold theta, and the BF16 values
+    either side, with both signs: the quotient x / S lands on the threshold
+    or just beside it.  Returns (rows, expected codes [rows, 128] uint8)."""
+    blocks = []  # list of (S, [(bf16 bits, code)] with 16 entries)
+    for c in range(1, 127):
+        S = e4m3fn_value(c)
+        items = []
+        for theta, tie, below, above in E2M1_TIES:
+            b = bf16_exact_bits(theta * S)
+            for bits, code in ((b, tie), (b - 1, below), (b + 1, above)):
+                for sign in (0, 0x8000):
+                    items.append((bits | sign, code | (8 if sign else 0)))
+        top = bf16_exact_bits(6 * S)
+        for k in range(0, len(items), 15):
+            chunk = items[k:k + 15]
+            chunk += [(0, 0)] * (15 - len(chunk))
+            blocks.append([(top, 7)] + chunk)
+    per_row = 7
+    n_rows = (len(blocks) + per_row - 1) // per_row
+    n_rows = (n_rows + 31) // 32 * 32
+    x = np.zeros((n_rows, 128), np.uint16)
+    codes = np.zeros((n_rows, 128), np.uint8)
+    for r in range(n_rows):
+        x[r, 0] = bf16_exact_bits(2688.0)
+        codes[r, 0] = 7  # 2688 / (448 * 1) = 6; the rest of block 0 is zero
+    for i, blk in enumerate(blocks):
+        r, b = divmod(i, per_row)
+        for j, (bits, code) in enumerate(blk):
+            x[r, 16 * (b + 1) + j] = bits
+            codes[r, 16 * (b + 1) + j] = code
+    return x, codes
+
+
+def unpack_codes(packed: np.ndarray) -> np.ndarray:
+    """[rows, cols/2] packed E2M1 bytes (element 2i in the low nibble) -> [rows, cols] codes."""
+    out = np.empty((packed.shape[0], packed.shape[1] * 2), np.uint8)
+    out[:, 0::2] = packed & 0xF
+    out[:, 1::2] = packed >> 4
+    return out

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import moe_workloads as W
-from tests.helpers import gemm_to_logical, scale_tie_rows, scale_tie_targets, to_dev, to_host
+from tests.helpers import code_tie_rows, gemm_to_logical, scale_tie_rows, scale_tie_targets, to_dev, to_host, unpack_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -162,3 +162,18 @@ def test_scale_encoder_ties(gpu, orc):
             assert np.array_equal(got[1], want[mode]), f"GPU scales vs the format, mode {mode} layout {layout}"
             _assert_same(got, ref, f"scale ties mode={mode} layout={layout}")
     print(f"  {len(scale_tie_targets())} block maxima at the E4M3 decision points, both roundings, both layouts")
+
+
+def test_code_decisions_at_every_scale(gpu, orc):
+    """E2M1 element codes at every decision point under each of the 126 E4M3
+    scales (quotients landing exactly on a threshold or a BF16 step beside
+    it, both signs): GPU equal to the format's expectation and to the oracle
+    bit for bit, both roundings and layouts."""
+    m, dev = gpu
+    x, want = code_tie_rows()
+    for mode in (0, 1):
+        ref = orc.quantize(x, mode)
+        for layout in (m.LAYOUT_LOGICAL, m.LAYOUT_GEMM):
+            got = _gpu_quant(m, dev, x, mode, layout)
+            assert np.array_equal(unpack_codes(got[0]), want), f"GPU codes vs the format, mode {mode} layout {layout}"
+            _assert_same(got, ref, f"code ties mode={mode} layout={layout}")

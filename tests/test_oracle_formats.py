@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from tests.exact import frac_to_bf16_bits
-from tests.helpers import scale_tie_rows
+from tests.helpers import code_tie_rows, scale_tie_rows, unpack_codes
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "nvfp4_hand_cases.json")
 
@@ -121,6 +121,20 @@ def test_quantizer_scale_decisions_through_rows(orc):
         _, sc, gg = orc.quantize(x, mode)
         assert np.array_equal(sc, want[mode]), f"mode {mode}: {np.argwhere(sc != want[mode])[:5].tolist()}"
         assert np.all(gg == g)
+
+
+def test_quantizer_code_decisions_through_rows(orc):
+    """The whole row path at every E2M1 decision point under every E4M3
+    scale: with a row maximum of 2688, g is exactly 1 and a block whose
+    maximum is 6 S gets the scale S, so theta * S (theta an E2M1 midpoint)
+    divides back to theta exactly; ties go to the even code, the BF16 values
+    beside them to the nearer code, and the sign bit is kept."""
+    x, want = code_tie_rows()
+    for mode in (0, 1):
+        c, _, g = orc.quantize(x, mode)
+        assert np.all(g == np.float32(1))
+        got = unpack_codes(c)
+        assert np.array_equal(got, want), f"mode {mode}: {np.argwhere(got != want)[:5].tolist()}"
 
 
 # --- Q: hand cases -----------------------------------------------------------------------------------
