@@ -73,19 +73,21 @@ __global__ void __launch_bounds__(256) quant_h_kernel(const uint16_t* __restrict
     }
     const int32_t pr = row2pair[row];
     // Row amax: the maxima are non-negative floats, which order like their
-    // bit patterns, so an integer max is exact.  They are read eight 16-byte
-    // vectors at a time, all in flight together (indices past the row's last
-    // vector re-read it).
+    // bit patterns, so an integer max is exact.  The two lanes of a row
+    // (lanes rl and rl + 32) each read half of every eight 16-byte vectors,
+    // all in flight together (indices past the row's last vector re-read
+    // it), and swap their partial maxima.
     const u32x4* part = reinterpret_cast<const u32x4*>(amax2_part + row * n_part);
     const int n4 = n_part / 4;
     uint32_t mbits = 0u;
     for (int i0 = 0; i0 < n4; i0 += 8) {
-        u32x4 q[8];
+        u32x4 q[4];
 #pragma unroll
-        for (int j = 0; j < 8; j++) q[j] = part[min(i0 + j, n4 - 1)];
+        for (int j = 0; j < 4; j++) q[j] = part[min(i0 + 4 * hh + j, n4 - 1)];
 #pragma unroll
-        for (int j = 0; j < 8; j++) mbits = max(mbits, max(max(q[j][0], q[j][1]), max(q[j][2], q[j][3])));
+        for (int j = 0; j < 4; j++) mbits = max(mbits, max(max(q[j][0], q[j][1]), max(q[j][2], q[j][3])));
     }
+    mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, 32, kWave));
     if (!row_tile_used(rt, E, capacity, expert_off, expert_count)) return;
     const bool valid = pr >= 0;  // padding rows are written as zeros
     const float amax = valid ? __uint_as_float(mbits) : 0.0f;
