@@ -239,4 +239,43 @@ __device__ __forceinline__ void quant_row_regs(const uint16_t* __restrict__ x, i
     if (lane == 0) gout[r] = rs.g;
 }
 
+// Several short rows per wavefront (cols % 32 == 0, at most LPR 32-element
+// groups per row): lane l quantizes group l % LPR of row r0 + l / LPR (rows at
+// or past `rows` are skipped), and a row's amax is reduced over its own LPR
+// lanes.  Same arithmetic and outputs as quant_row_regs; a row of 24 groups
+// (768 columns) then keeps 48 of 64 lanes busy instead of 24.
+template <int LPR>
+__device__ __forceinline__ void quant_rows_packed(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                  int64_t ld, int64_t r0, bool round_up, bool gemm,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                  float* __restrict__ gout) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t r = r0 + lane / LPR;
+    const int gi = lane % LPR;
+    const bool on = r < rows && gi < (cols >> 5);
+    u32x4 v[4];
+    uint32_t m = 0u;
+    if (on) {
+        load32(x + r * ld + gi * 32, false, v);
+        m = max(max(absmax8_bits(v[0]), absmax8_bits(v[1])), max(absmax8_bits(v[2]), absmax8_bits(v[3])));
+    }
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
+    const RowScale rs = row_scale(bf16_to_f32(m));
+    if (on) {
+        u32x4 c;
+        uint32_t s2;
+        quant32(v, rs, round_up, false, c, s2);
+        const int64_t k = (int64_t)gi * 32;
+        if (gemm) {
+            *reinterpret_cast<u32x4*>(codes + gemm_code_off(r, k, cols)) = c;
+            *reinterpret_cast<uint16_t*>(scales + gemm_scale_off(r, k, cols)) = (uint16_t)s2;
+        } else {
+            *reinterpret_cast<u32x4*>(codes + r * (cols >> 1) + gi * 16) = c;
+            *reinterpret_cast<uint16_t*>(scales + r * (cols >> 4) + gi * 2) = (uint16_t)s2;
+        }
+    }
+    if (gi == 0 && r < rows) gout[r] = rs.g;
+}
+
 }  // namespace nvfp4

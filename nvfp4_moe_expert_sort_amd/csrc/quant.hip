@@ -7,7 +7,9 @@
 // and writes 16 bytes of codes.
 //   quant_rows_kernel  one wave per row (generic entry point, weights, dense X);
 //                      rows of up to 8192 columns are read once into registers,
-//                      longer ones in two passes (amax, then quantize);
+//                      longer ones in two passes (amax, then quantize); rows of
+//                      at most 1024 columns (a multiple of 32) go 2, 4 or 8 to
+//                      a wave;
 //   quant_h_kernel     FC2 input: one wave per (32-row tile, 128 columns) of
 //                      the sorted buffer, writing whole 1 KiB GEMM chunks; the
 //                      row amax is the max of the per-32-column maxima the FC1
@@ -22,11 +24,21 @@ namespace nvfp4 {
 __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                          int64_t ld, uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ scales, float* __restrict__ g,
-                                                         int gemm, int round_up) {
+                                                         int gemm, int round_up, int rows_per_wave) {
+    const bool ru = round_up != 0, gm = gemm != 0;
+    if (rows_per_wave > 1) {  // short rows, several per wavefront
+        const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * rows_per_wave;
+        if (r0 >= rows) return;
+        switch (rows_per_wave) {
+            case 2: quant_rows_packed<32>(x, rows, cols, ld, r0, ru, gm, codes, scales, g); break;
+            case 4: quant_rows_packed<16>(x, rows, cols, ld, r0, ru, gm, codes, scales, g); break;
+            default: quant_rows_packed<8>(x, rows, cols, ld, r0, ru, gm, codes, scales, g); break;
+        }
+        return;
+    }
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const uint16_t* xr = x + row * ld;
-    const bool ru = round_up != 0, gm = gemm != 0;
     // Rows of up to 8192 columns (cols % 32 == 0) are read once into registers.
     const int64_t per_lane = (cols % 32 == 0) ? (cols / 32 + kWave - 1) / kWave : 0;
     switch (per_lane) {
@@ -114,9 +126,13 @@ __global__ void __launch_bounds__(256) quant_h_kernel(const uint16_t* __restrict
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
                              uint8_t* scales, float* g, bool gemm, bool round_up, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
-    const int64_t blocks = (rows + 3) / 4;
+    // Rows of at most 32 groups of 32 elements share a wavefront: 2, 4 or 8
+    // rows of up to 32, 16 or 8 groups.
+    const int64_t groups = cols / 32;
+    const int rpw = (cols % 32 != 0 || groups > 32) ? 1 : groups > 16 ? 2 : groups > 8 ? 4 : 8;
+    const int64_t blocks = (rows + 4 * rpw - 1) / (4 * rpw);
     hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, cols, ld, codes,
-                       scales, g, gemm ? 1 : 0, round_up ? 1 : 0);
+                       scales, g, gemm ? 1 : 0, round_up ? 1 : 0, rpw);
     return hipGetLastError();
 }
 
