@@ -86,15 +86,17 @@ def test_hand_cases(gpu, orc):
 
 
 @pytest.mark.parametrize("mode", [0, 1])
-@pytest.mark.parametrize("cols", [16, 128, 256, 768, 2048])
+@pytest.mark.parametrize("cols", [16, 32, 128, 256, 512, 768, 1024, 1056, 2048])
 def test_random_rows_logical(gpu, orc, mode, cols):
+    # Rows of at most 1024 columns go 8, 4 or 2 to a wavefront (up to 256, 512
+    # and 1024 columns); 1056 is the shortest row with a wavefront of its own.
     m, dev = gpu
-    x = _rows(100 + cols, 13, cols)  # 65 rows: not a multiple of the 4 rows per block
+    x = _rows(100 + cols, 13, cols)  # 65 rows: no multiple of the rows per block in any path
     _assert_same(_gpu_quant(m, dev, x, mode, m.LAYOUT_LOGICAL), orc.quantize(x, mode), f"cols={cols} mode={mode}")
 
 
 @pytest.mark.parametrize("mode", [0, 1])
-@pytest.mark.parametrize("cols", [128, 768, 2048])
+@pytest.mark.parametrize("cols", [128, 512, 768, 1024, 2048])
 def test_random_rows_gemm_layout(gpu, orc, mode, cols):
     m, dev = gpu
     x = _rows(200 + cols, 32, cols)[:160]
