@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-w4a16", action="store_true", help="skip the W4A16 variant's forwards")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense NVFP4 linear")
     ap.add_argument("--no-skewed", action="store_true", help="skip the skewed-routing T = 16384 forwards")
+    ap.add_argument("--no-router", action="store_true", help="skip the on-device router (scores + top-k)")
+    ap.add_argument("--no-masked", action="store_true", help="skip the masked fixed-capacity forward")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -269,6 +271,54 @@ def main():
                "tflops": 2.0 * T * K * 3 * H * I / (w16_ms / 1e3) / 1e12,
                "what": "NVFP4 weights x BF16 activations (bf16 MFMA), same routing, producer and combine"}
 
+    # The masked fixed-capacity layout (secondary): the same forward with expert
+    # e's rows in the fixed chunk [e*capacity, (e+1)*capacity), capacity the
+    # smallest multiple of 32 that holds the workload's busiest expert.
+    masked = None
+    if not args.no_masked:
+        cap = int(-(-int(wl.expert_counts().max()) // 32) * 32)
+        ws_m = m.alloc_workspace_masked(cfg, cap, dev)
+        for _ in range(20):
+            m.moe_expert_forward_masked(cfg, cap, x, ids, probs, qw, ws_m, out=out)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(50):
+            m.moe_expert_forward_masked(cfg, cap, x, ids, probs, qw, ws_m, out=out, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        mk_ms = ev[0].elapsed_time(ev[1]) / 50
+        masked = {"capacity": cap, "ms_per_step": mk_ms, "tokens_per_s": T / (mk_ms / 1e3),
+                  "what": "same workload, expert rows in fixed chunks of `capacity` (static-capacity layout)"}
+        del ws_m
+
+    # The on-device router (secondary): FP32 scores of x against a [E, H] BF16
+    # router weight (N(0, 0.02^2), seed 21) and the deterministic top-k with
+    # renormalised probabilities, for the whole batch and at decode sizes.
+    router = None
+    if not args.no_router:
+        rng = np.random.default_rng(21)
+        w_r = torch.from_numpy(W.f32_to_bf16_bits((rng.standard_normal((E, H)) * 0.02).astype(np.float32))
+                               .view(np.int16)).to(dev)
+        router = {}
+        for n in (T, 64, 1):
+            xs = x[:n].contiguous()
+            bufs = (torch.empty((n, E), dtype=torch.float32, device=dev),
+                    torch.empty((n, K), dtype=torch.int32, device=dev),
+                    torch.empty((n, K), dtype=torch.float32, device=dev))
+            for _ in range(20):
+                m.router_topk(xs, w_r, K, out=bufs)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(100):
+                m.router_topk(xs, w_r, K, stream=stream, out=bufs)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            r_us = ev[0].elapsed_time(ev[1]) / 100 * 1e3
+            r_bytes = n * H * 2 + E * H * 2 + n * E * 4 + n * K * 8
+            router[f"T{n}"] = {"us": r_us, "tflops": 2.0 * n * H * E / (r_us / 1e6) / 1e12,
+                               "GB_s": r_bytes / (r_us / 1e6) / 1e9}
+        del w_r
+
     # Decode-sized forwards (secondary): the first n tokens of the workload, one
     # forward captured into a HIP graph and replayed back to back, and the same
     # forward launched eagerly; microseconds per forward.
@@ -345,6 +395,10 @@ def main():
     }
     if decode:
         result["decode"] = decode
+    if masked:
+        result["masked"] = masked
+    if router:
+        result["router"] = router
     if w16:
         result["w4a16"] = w16
     if dense:

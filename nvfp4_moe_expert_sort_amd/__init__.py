@@ -265,15 +265,18 @@ def device_error(cfg: Config, workspace, stream=None) -> int:
     return code.value
 
 
-def router_topk(x, w_router, k: int, renormalize: bool = True, stream=None):
+def router_topk(x, w_router, k: int, renormalize: bool = True, stream=None, out=None):
     """nvfp4moe_router_topk: x [T,H] BF16, w_router [E,H] BF16 -> (logits [T,E] f32, ids [T,k] int32,
-    probs [T,k] f32)."""
+    probs [T,k] f32); `out` may hold the three output tensors, preallocated."""
     import torch
     T, H = x.shape
     E = w_router.shape[0]
-    logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
-    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
-    probs = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if out is not None:
+        logits, ids, probs = out
+    else:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+        ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        probs = torch.empty((T, k), dtype=torch.float32, device=x.device)
     st = lib().nvfp4moe_router_topk(_ptr(x), T, H, _ptr(w_router), E, k, 1 if renormalize else 0, _ptr(logits),
                                     _ptr(ids), _ptr(probs), _stream(stream))
     _check(st, "nvfp4moe_router_topk")

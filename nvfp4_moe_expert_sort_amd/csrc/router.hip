@@ -14,10 +14,11 @@
 //            memory (16 contiguous bytes per lane).  A token's scores come
 //            from the same instruction sequence whatever T is and wherever
 //            the token sits in its tile.
-//   phase 2  per token (one wavefront): K rounds of a wave-wide maximum of
-//            64-bit keys (order-preserving score bits, then the complement of
-//            the expert id, so equal scores go to the lower id); slot k gets
-//            the k-th expert of that total order.  Probabilities are the
+//   phase 2  per token (one wavefront): 64-bit keys (order-preserving score
+//            bits, then the complement of the expert id, so equal scores go
+//            to the lower id); slot k gets the k-th expert of that total
+//            order.  Up to 256 experts each key's rank is counted against all
+//            keys at once; beyond that, K rounds of a wave-wide maximum.  Probabilities are the
 //            softmax restricted to the selection (renormalize) or over all
 //            experts, in FP32 with one fixed summation order.
 #include "nvfp4_device.h"
@@ -29,6 +30,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRouterTok = 32;                        // tokens per workgroup (one MFMA row tile)
 constexpr int kRouterKeys = kMaxExperts / kWave;      // scores per lane in phase 2
+constexpr int kRankMaxE = 256;                        // phase 2 ranks by counting up to this many experts
 
 // Unsigned integer whose order is the order of the FP32 value (-0 and +0 equal).
 __device__ __forceinline__ uint32_t score_order(float v) {
@@ -87,6 +89,9 @@ __global__ void __launch_bounds__(256) router_kernel(const uint16_t* __restrict_
     __syncthreads();  // this workgroup's scores are written (workgroup-scope fence included)
 
     // Phase 2: wave w takes tokens w, w + 4, ... of the tile.
+    __shared__ uint64_t skey[4][kRankMaxE];
+    __shared__ uint64_t ssel[4][kMaxTopK];
+    const bool by_rank = E <= kRankMaxE;
     for (int tl = wave; tl < kRouterTok; tl += 4) {
         const int64_t t = t0 + tl;
         if (t >= T) break;
@@ -99,7 +104,43 @@ __global__ void __launch_bounds__(256) router_kernel(const uint16_t* __restrict_
         }
         int my_e = 0;
         float my_l = 0.0f;
-        for (int k = 0; k < K; k++) {
+        if (by_rank) {
+            // The keys are unique, so a key's place in the order is the number
+            // of larger keys; slot k takes the key of rank k.  Every lane
+            // counts against all E keys (read back through LDS as broadcasts),
+            // so no round waits on another.
+            constexpr int kR = kRankMaxE / kWave;
+#pragma unroll
+            for (int i = 0; i < kR; i++) {
+                const int e = i * kWave + lane;
+                if (e < E) skey[wave][e] = key[i];
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
+            __builtin_amdgcn_wave_barrier();
+            int rank[kR];
+#pragma unroll
+            for (int i = 0; i < kR; i++) rank[i] = 0;
+            for (int j = 0; j < E; j++) {
+                const uint64_t kj = skey[wave][j];
+#pragma unroll
+                for (int i = 0; i < kR; i++) rank[i] += kj > key[i] ? 1 : 0;
+            }
+#pragma unroll
+            for (int i = 0; i < kR; i++) {
+                const int e = i * kWave + lane;
+                if (e < E && rank[i] < K) ssel[wave][rank[i]] = key[i];
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+            if (lane < K) {
+                const uint64_t b = ssel[wave][lane];
+                my_e = (int)~(uint32_t)b;
+                my_l = score_value((uint32_t)(b >> 32));
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // read before the next token's keys overwrite them
+            __builtin_amdgcn_wave_barrier();
+        }
+        for (int k = 0; !by_rank && k < K; k++) {
             uint64_t best = 0ull;
 #pragma unroll
             for (int i = 0; i < kRouterKeys; i++) best = key[i] > best ? key[i] : best;
