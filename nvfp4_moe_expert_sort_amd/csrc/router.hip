@@ -42,6 +42,18 @@ __device__ __forceinline__ float score_value(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
+// rank[i] = the number of the E keys in sk (zero-padded to an even count)
+// larger than key[i], for this lane's first NK keys.
+template <int NK>
+__device__ __forceinline__ void count_ranks(const uint64_t* sk, int E2, const uint64_t* key, int* rank) {
+    for (int j = 0; j < E2; j += 2) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(sk + j);  // two keys, one broadcast read
+        const uint64_t k0 = ((uint64_t)kv[1] << 32) | kv[0], k1 = ((uint64_t)kv[3] << 32) | kv[2];
+#pragma unroll
+        for (int i = 0; i < NK; i++) rank[i] += (k0 > key[i] ? 1 : 0) + (k1 > key[i] ? 1 : 0);
+    }
+}
+
 __global__ void __launch_bounds__(256) router_kernel(const uint16_t* __restrict__ x, int32_t T, int32_t H,
                                                      const uint16_t* __restrict__ w, int32_t E, int32_t K,
                                                      int renorm, float* __restrict__ logits,
@@ -89,7 +101,7 @@ __global__ void __launch_bounds__(256) router_kernel(const uint16_t* __restrict_
     __syncthreads();  // this workgroup's scores are written (workgroup-scope fence included)
 
     // Phase 2: wave w takes tokens w, w + 4, ... of the tile.
-    __shared__ uint64_t skey[4][kRankMaxE];
+    __shared__ __attribute__((aligned(16))) uint64_t skey[4][kRankMaxE];
     __shared__ uint64_t ssel[4][kMaxTopK];
     const bool by_rank = E <= kRankMaxE;
     for (int tl = wave; tl < kRouterTok; tl += 4) {
@@ -109,22 +121,28 @@ __global__ void __launch_bounds__(256) router_kernel(const uint16_t* __restrict_
             // of larger keys; slot k takes the key of rank k.  Every lane
             // counts against all E keys (read back through LDS as broadcasts),
             // so no round waits on another.
+            // Only the lane's live keys are ranked (ceil(E / 64) of them), two
+            // keys per LDS read (an odd E is padded with a zero key, which
+            // never outranks a real one).
             constexpr int kR = kRankMaxE / kWave;
+            const int E2 = (E + 1) & ~1;
 #pragma unroll
             for (int i = 0; i < kR; i++) {
                 const int e = i * kWave + lane;
-                if (e < E) skey[wave][e] = key[i];
+                if (e < E2) skey[wave][e] = e < E ? key[i] : 0ull;
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
             __builtin_amdgcn_wave_barrier();
             int rank[kR];
 #pragma unroll
             for (int i = 0; i < kR; i++) rank[i] = 0;
-            for (int j = 0; j < E; j++) {
-                const uint64_t kj = skey[wave][j];
-#pragma unroll
-                for (int i = 0; i < kR; i++) rank[i] += kj > key[i] ? 1 : 0;
-            }
+            const int nk = (E + kWave - 1) / kWave;
+            if (nk == 1)
+                count_ranks<1>(&skey[wave][0], E2, key, rank);
+            else if (nk == 2)
+                count_ranks<2>(&skey[wave][0], E2, key, rank);
+            else
+                count_ranks<4>(&skey[wave][0], E2, key, rank);
 #pragma unroll
             for (int i = 0; i < kR; i++) {
                 const int e = i * kWave + lane;
