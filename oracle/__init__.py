@@ -90,7 +90,11 @@ def _load():
     lib.orc_moe_forward_deq.restype = None
     lib.orc_moe_forward_deq.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P, P, ctypes.c_int, P, P, P, P, P]
     lib.orc_moe_forward_w4a16.restype = None
-    lib.orc_moe_forward_w4a16.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P]
+    lib.orc_moe_forward_w4a16.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P]
+    lib.orc_moe_fc2.restype = None
+    lib.orc_moe_fc2.argtypes = [P, I64, I64, I64, P, P, P, ctypes.c_int, ctypes.c_int, P]
+    lib.orc_route_masked.restype = I64
+    lib.orc_route_masked.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P]
     lib.orc_moe_forward.restype = None
     lib.orc_moe_forward.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, ctypes.c_int, P, P, P,
                                     P, P]
@@ -227,10 +231,49 @@ def route(ids: np.ndarray, n_experts: int, m_align: int):
     return off, pair2row, row2pair[:P_pad].copy()
 
 
+def route_masked(ids: np.ndarray, n_experts: int, m_align: int, capacity: int):
+    """Expected masked fixed-capacity layout (article, section 4.4, "two layouts,
+    same row results"): expert e owns rows [e*capacity, (e+1)*capacity).
+
+    Returns (off [E+1] int64, pair2row [T*K] int32 (-1: no row, past the
+    capacity), row2pair [E*capacity] int32 (-1: padding or unused),
+    row_used [E*capacity] bool (kept and padding rows), n_dropped)."""
+    ids = _c(ids, np.int32)
+    T, K = ids.shape
+    off = np.empty((n_experts + 1,), np.int64)
+    pair2row = np.empty((T * K,), np.int32)
+    row2pair = np.empty((n_experts * capacity,), np.int32)
+    used = np.empty((n_experts * capacity,), np.uint8)
+    n = _load().orc_route_masked(_p(ids), T, K, n_experts, m_align, capacity, _p(off), _p(pair2row), _p(row2pair),
+                                 _p(used))
+    if n == -1:
+        raise ValueError("expert id out of range")
+    if n == -2:
+        raise ValueError("capacity must be a positive multiple of m_align")
+    return off, pair2row, row2pair, used.astype(bool), int(n)
+
+
+def moe_fc2(h_pairs, ids, weights: "DequantWeights", quantize_h: bool = True, mode: int = SCALE_RU):
+    """FC2 alone from a given h, one row per pair p = t*K + k (miniTE page, "how
+    it differs": FC2 on Q(h) with the same epilogue; quantize_h False: the
+    W4A16 variant's unquantized BF16 h).  The arithmetic is the layer's own
+    FC2 step.  Returns y2 [P, H] BF16 bits."""
+    h = _c(h_pairs, np.uint16)
+    ids = _c(ids, np.int32).reshape(-1)
+    P, I = h.shape
+    assert ids.size == P and I == weights.I
+    if ids.size and (ids.min() < 0 or ids.max() >= weights.E):
+        raise ValueError("expert id out of range")
+    y2 = np.empty((P, weights.H), np.uint16)
+    _load().orc_moe_fc2(_p(h), P, I, weights.H, _p(ids), _p(weights.d2), _p(weights.g2), 1 if quantize_h else 0,
+                        int(mode), _p(y2))
+    return y2
+
+
 def moe_forward_w4a16(x_bf16, ids, probs, weights: DequantWeights, intermediates: bool = False):
     """The W4A16 variant (article, section 6: NVFP4 W4A16 routed experts): NVFP4
     weights, BF16 activations not quantized; epilogues multiply by g^w only.
-    Returns out [T,H] BF16 bits, and with ``intermediates`` per-pair h [P,I], y2 [P,H]."""
+    Returns out [T,H] BF16 bits, and with ``intermediates`` per-pair y1 [P,2I], h [P,I], y2 [P,H]."""
     x = _c(x_bf16, np.uint16)
     ids = _c(ids, np.int32)
     probs = _c(probs, np.float32)
@@ -242,12 +285,13 @@ def moe_forward_w4a16(x_bf16, ids, probs, weights: DequantWeights, intermediates
         raise ValueError("expert id out of range")
     P = T * K
     out = np.empty((T, H), np.uint16)
+    y1 = np.empty((P, 2 * I), np.uint16) if intermediates else None
     h = np.empty((P, I), np.uint16) if intermediates else None
     y2 = np.empty((P, H), np.uint16) if intermediates else None
     _load().orc_moe_forward_w4a16(_p(x), T, H, I, K, _p(ids), _p(probs), _p(weights.d1), _p(weights.g1),
-                                  _p(weights.d2), _p(weights.g2), _p(out), _p(h), _p(y2))
+                                  _p(weights.d2), _p(weights.g2), _p(out), _p(y1), _p(h), _p(y2))
     if intermediates:
-        return out, dict(h=h, y2=y2)
+        return out, dict(y1=y1, h=h, y2=y2)
     return out
 
 

@@ -330,6 +330,50 @@ int64_t orc_route(const int32_t* ids, int64_t T, int64_t K, int64_t E, int64_t m
     return P_pad;
 }
 
+/* The masked fixed-capacity layout (article, section 4.4, "two layouts, same
+ * row results": the decode side hands the expert GEMMs per-expert chunks of a
+ * fixed capacity, the training side packed rows).  Expert e owns the chunk of
+ * rows [e*capacity, (e+1)*capacity), so off[e] = e*capacity.  Its pairs take
+ * the chunk's rows in increasing p, as in the contiguous layout; a pair whose
+ * rank within its expert is capacity or more gets no row (pair2row = -1).
+ * The kept rows are followed by padding rows (-1) up to a multiple of
+ * m_align; row_used[r] is 1 for kept and padding rows, 0 for the rest of the
+ * chunk, which holds nothing.  row2pair and row_used have E*capacity entries.
+ * Returns the number of pairs left without a row, -1 if an id is outside
+ * [0, E), -2 if capacity is not a positive multiple of m_align. */
+int64_t orc_route_masked(const int32_t* ids, int64_t T, int64_t K, int64_t E, int64_t m_align, int64_t capacity,
+                         int64_t* off, int32_t* pair2row, int32_t* row2pair, uint8_t* row_used) {
+    int64_t P = T * K;
+    if (capacity <= 0 || capacity % m_align != 0) return -2;
+    for (int64_t p = 0; p < P; p++)
+        if (ids[p] < 0 || ids[p] >= E) return -1;
+    int64_t* rank = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    for (int64_t e = 0; e <= E; e++) off[e] = e * capacity;
+    for (int64_t r = 0; r < E * capacity; r++) {
+        row2pair[r] = -1;
+        row_used[r] = 0;
+    }
+    int64_t dropped = 0;
+    for (int64_t p = 0; p < P; p++) {
+        int64_t e = ids[p];
+        int64_t i = rank[e]++;
+        if (i >= capacity) {
+            pair2row[p] = -1;
+            dropped++;
+            continue;
+        }
+        pair2row[p] = (int32_t)(off[e] + i);
+        row2pair[off[e] + i] = (int32_t)p;
+    }
+    for (int64_t e = 0; e < E; e++) {
+        int64_t kept = rank[e] < capacity ? rank[e] : capacity;
+        int64_t padded = (kept + m_align - 1) / m_align * m_align;
+        for (int64_t i = 0; i < padded; i++) row_used[off[e] + i] = 1;
+    }
+    free(rank);
+    return dropped;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Router (the step before the path)                                         */
 /* ------------------------------------------------------------------------ */
@@ -383,6 +427,51 @@ void orc_router_topk(const float* logits, int64_t T, int64_t E, int64_t K, int r
 /* The layer                                                                 */
 /* ------------------------------------------------------------------------ */
 
+/* FC2 of one pair: y2 = bf16((a . W2[e]^T) g^a g^w2) over the H rows of W2[e].
+ * quantize_h != 0 (the NVFP4 layer): a = Q(h) dequantized and g^a its outer
+ * scale, Q taken on the BF16 h that FC2 consumes; quantize_h == 0 (W4A16):
+ * a = the BF16 values of h and g^a = 1.  w2d: E matrices [H][I] of
+ * dequantized weights, w2g their outer scales.  hc, hs, hd: scratch of I/2,
+ * I/16 bytes and I doubles. */
+static void fc2_pair(const uint16_t* h, int64_t I, int64_t H, int64_t e, const double* w2d, const float* w2g,
+                     int quantize_h, int mode, uint8_t* hc, uint8_t* hs, double* hd, uint16_t* y2) {
+    double gh = 1.0;
+    if (quantize_h) {
+        float g;
+        orc_quantize_row(h, I, mode, hc, hs, &g);
+        orc_dequantize(hc, hs, 1, I, hd);
+        gh = (double)g;
+    } else {
+        for (int64_t k = 0; k < I; k++) hd[k] = orc_bf16_to_double(h[k]);
+    }
+    for (int64_t m = 0; m < H; m++) {
+        int64_t wr = e * H + m;
+        const double* w = w2d + wr * I;
+        double acc = 0.0;
+        for (int64_t k = 0; k < I; k++) acc += hd[k] * w[k];
+        y2[m] = orc_double_to_bf16(acc * gh * (double)w2g[wr]);
+    }
+}
+
+/* The FC2 step alone, from a given h: y2[p] = fc2_pair(h[p], expert ids[p])
+ * for P pairs (h [P][I] BF16, y2 [P][H] BF16), with the same arithmetic as
+ * the layers below.  Lets a test run FC2 on another implementation's h. */
+void orc_moe_fc2(const uint16_t* h, int64_t P, int64_t I, int64_t H, const int32_t* ids, const double* w2d,
+                 const float* w2g, int quantize_h, int mode, uint16_t* y2) {
+#pragma omp parallel
+    {
+        uint8_t* hc = (uint8_t*)malloc((size_t)(I / 2));
+        uint8_t* hs = (uint8_t*)malloc((size_t)(I / 16));
+        double* hd = (double*)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t p = 0; p < P; p++)
+            fc2_pair(h + p * I, I, H, ids[p], w2d, w2g, quantize_h, mode, hc, hs, hd, y2 + p * H);
+        free(hc);
+        free(hs);
+        free(hd);
+    }
+}
+
 /* NVFP4 MoE expert forward for T tokens, computed per (token, slot) pair with
  * no sorting (the sorted layout changes no value):
  *   Xq = Q(x[t])                                   per token
@@ -429,18 +518,8 @@ void orc_moe_forward_deq(const uint16_t* x, int64_t T, int64_t H, int64_t I, int
             /* router-weighted SwiGLU producer */
             float amax2;
             orc_swiglu_prob(y1, probs + p, 1, I, h, &amax2);
-            /* FC2 input quantization: Q on the BF16 h that FC2 consumes */
-            float gh;
-            orc_quantize_row(h, I, mode, hc, hs, &gh);
-            orc_dequantize(hc, hs, 1, I, hd);
-            /* FC2 */
-            for (int64_t m = 0; m < H; m++) {
-                int64_t wr = e * H + m;
-                const double* w = w2d + wr * I;
-                double acc = 0.0;
-                for (int64_t k = 0; k < I; k++) acc += hd[k] * w[k];
-                y2[p * H + m] = orc_double_to_bf16(acc * (double)gh * (double)w2g[wr]);
-            }
+            /* FC2 on Q(h), Q taken on the BF16 h that FC2 consumes */
+            fc2_pair(h, I, H, e, w2d, w2g, 1, mode, hc, hs, hd, y2 + p * H);
             if (y1_out) memcpy(y1_out + p * 2 * I, y1, sizeof(uint16_t) * (size_t)(2 * I));
             if (h_out) memcpy(h_out + p * I, h, sizeof(uint16_t) * (size_t)I);
             if (amax2_out) amax2_out[p] = amax2;
@@ -470,10 +549,10 @@ void orc_moe_forward_deq(const uint16_t* x, int64_t T, int64_t H, int64_t I, int
  *   y2 = bf16((h . W2q[e]^T) g^w2)               [H]
  *   out[t] = bf16(FP32 sum over k of y2[t,k])
  * Weights as for orc_moe_forward_deq; optional per-pair outputs (NULL to
- * skip): h [P][I], y2 [P][H]. */
+ * skip): y1 [P][2I], h [P][I], y2 [P][H]. */
 void orc_moe_forward_w4a16(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t K, const int32_t* ids,
                            const float* probs, const double* w1d, const float* w1g, const double* w2d,
-                           const float* w2g, uint16_t* out, uint16_t* h_out, uint16_t* y2_out) {
+                           const float* w2g, uint16_t* out, uint16_t* y1_out, uint16_t* h_out, uint16_t* y2_out) {
     int64_t P = T * K;
     uint16_t* y2 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(P * H));
 #pragma omp parallel
@@ -495,14 +574,8 @@ void orc_moe_forward_w4a16(const uint16_t* x, int64_t T, int64_t H, int64_t I, i
             }
             float amax2;
             orc_swiglu_prob(y1, probs + p, 1, I, h, &amax2);
-            for (int64_t k = 0; k < I; k++) hd[k] = orc_bf16_to_double(h[k]);
-            for (int64_t m = 0; m < H; m++) {
-                int64_t wr = e * H + m;
-                const double* w = w2d + wr * I;
-                double acc = 0.0;
-                for (int64_t k = 0; k < I; k++) acc += hd[k] * w[k];
-                y2[p * H + m] = orc_double_to_bf16(acc * (double)w2g[wr]);
-            }
+            fc2_pair(h, I, H, e, w2d, w2g, 0, 0, NULL, NULL, hd, y2 + p * H);
+            if (y1_out) memcpy(y1_out + p * 2 * I, y1, sizeof(uint16_t) * (size_t)(2 * I));
             if (h_out) memcpy(h_out + p * I, h, sizeof(uint16_t) * (size_t)I);
         }
         free(a);

@@ -157,6 +157,53 @@ def test_route_properties(orc):
         orc.route(np.array([[0, 9]], np.int32), 8, 32)
 
 
+def test_route_masked_hand_example(orc):
+    """Masked fixed-capacity layout (article, section 4.4: per-expert chunks of
+    a fixed capacity), worked by hand.  Pairs p = t*K + k of ids below go to
+    expert 0: p = 1, 4, 7; expert 1: p = 3; expert 2: p = 0, 2, 5, 6."""
+    ids = np.array([[2, 0], [2, 1], [0, 2], [2, 0]], np.int32)
+    off, p2r, r2p, used, dropped = orc.route_masked(ids, 3, 2, 4)
+    assert off.tolist() == [0, 4, 8, 12] and dropped == 0
+    assert p2r.tolist() == [8, 0, 9, 4, 1, 10, 11, 2]
+    #                 expert 0 chunk    expert 1 chunk     expert 2 chunk
+    assert r2p.tolist() == [1, 4, 7, -1, 3, -1, -1, -1, 0, 2, 5, 6]
+    assert used.tolist() == [1, 1, 1, 1, 1, 1, 0, 0, 1, 1, 1, 1]
+    # capacity 2: the third and later pairs of an expert get no row
+    off, p2r, r2p, used, dropped = orc.route_masked(ids, 3, 2, 2)
+    assert off.tolist() == [0, 2, 4, 6] and dropped == 3
+    assert p2r.tolist() == [4, 0, 5, 2, 1, -1, -1, -1]
+    assert r2p.tolist() == [1, 4, 3, -1, 0, 2]
+    assert used.tolist() == [1, 1, 1, 1, 1, 1]
+    with pytest.raises(ValueError):
+        orc.route_masked(ids, 3, 2, 3)  # not a multiple of m_align
+    with pytest.raises(ValueError):
+        orc.route_masked(np.array([[0, 3]], np.int32), 3, 2, 4)
+
+
+def test_route_masked_matches_contiguous_order(orc):
+    """With a capacity that holds every expert, each expert's rows are the
+    contiguous layout's rows moved to the start of its chunk (same order)."""
+    wl = W.skewed(T=512)
+    E, A = wl.shape.E, 32
+    off_c, p2r_c, _ = orc.route(wl.ids, E, A)
+    cap = int(np.diff(off_c).max())
+    off, p2r, r2p, used, dropped = orc.route_masked(wl.ids, E, A, cap)
+    assert dropped == 0 and np.array_equal(off, np.arange(E + 1) * cap)
+    e = wl.ids.reshape(-1)
+    assert np.array_equal(p2r, e * cap + (p2r_c - off_c[e]))
+    assert np.array_equal(r2p[p2r], np.arange(e.size))
+    cnt = wl.expert_counts()
+    pad = (cnt + A - 1) // A * A
+    assert np.array_equal(used.reshape(E, cap).sum(axis=1), pad)
+    # a smaller capacity keeps each expert's first pairs, in the same order
+    cap2 = 64
+    off, p2r2, r2p2, used2, dropped2 = orc.route_masked(wl.ids, E, A, cap2)
+    rank = p2r_c - off_c[e]
+    assert dropped2 == int((rank >= cap2).sum()) > 0
+    assert np.array_equal(p2r2[rank < cap2], e[rank < cap2] * cap2 + rank[rank < cap2])
+    assert np.all(p2r2[rank >= cap2] == -1)
+
+
 # --- the layer ---------------------------------------------------------------------------------------
 
 def _tiny_layer(seed=0, T=6, H=64, E=3, K=2, I=32):
@@ -189,6 +236,42 @@ def test_layer_wiring_matches_pinned_primitives(orc):
             assert np.array_equal(y2[0], mid["y2"][t * K + k])
             y2_pairs[t, k] = y2[0]
     assert np.array_equal(out, orc.combine(y2_pairs))
+
+
+def test_fc2_stage_exact_bruteforce(orc):
+    """moe_fc2 (FC2 alone from a given h) against exact rationals: Q(h) per
+    pair, dequantized values, sum over k, times g^h g^w2, one BF16 rounding;
+    and on the layer's own h it returns the layer's y2 bit for bit (both
+    routings of the activations: quantized for NVFP4, BF16 for W4A16)."""
+    wl, w1, w2 = _tiny_layer(seed=3, T=4, H=32, E=3, K=2, I=32)
+    wts = orc.DequantWeights(w1, w2)
+    out, mid = orc.moe_forward(wl.x, wl.ids, wl.probs, wts, intermediates=True)
+    y2 = orc.moe_fc2(mid["h"], wl.ids, wts)
+    assert np.array_equal(y2, mid["y2"])
+    H, I = wl.shape.H, wl.shape.I
+    e_of = wl.ids.reshape(-1)
+    boundary = 0
+    for p in range(e_of.size):
+        hc, hs, gh = orc.quantize(mid["h"][p:p + 1])
+        a = orc.dequantize(hc, hs)[0]
+        e = int(e_of[p])
+        for m in range(H):
+            acc = sum(Fraction(float(a[k])) * Fraction(float(wts.d2[e * H + m, k])) for k in range(I))
+            exact = acc * f32_to_frac(gh[0]) * f32_to_frac(wts.g2[e * H + m])
+            if near_bf16_boundary(exact):
+                boundary += 1
+                continue
+            assert int(y2[p, m]) == frac_to_bf16_bits(exact), (p, m)
+    assert boundary == 0
+    # W4A16: FC2 on the BF16 h itself
+    out16, mid16 = orc.moe_forward_w4a16(wl.x, wl.ids, wl.probs, wts, intermediates=True)
+    y2b = orc.moe_fc2(mid16["h"], wl.ids, wts, quantize_h=False)
+    assert np.array_equal(y2b, mid16["y2"])
+    p, m = 5, 7
+    e = int(e_of[p])
+    exact = sum(bf16_bits_to_frac(mid16["h"][p, k]) * Fraction(float(wts.d2[e * H + m, k])) for k in range(I))
+    exact *= f32_to_frac(wts.g2[e * H + m])
+    assert near_bf16_boundary(exact) or int(y2b[p, m]) == frac_to_bf16_bits(exact)
 
 
 def test_layer_tokens_are_independent(orc):
