@@ -7,9 +7,17 @@ quantize h, FC2, combine) over the Qwen3-30B-A3B-shaped layer with 4096
 tokens (hidden 2048, 128 experts, top-8, expert intermediate 768; synthetic
 seeded inputs and random weights, resident in HBM before timing).  W untimed
 warm-up steps, then exactly K steps bracketed by device synchronisation.
-Prints one JSON line.  The dominant kernel (FC1) is timed live inside the
-timed region with HIP events recorded on the forward's stream at its
-boundaries; the CPU oracle is timed on a bounded sample on the host cores.
+Prints one JSON line.  The dominant kernel (FC1) is timed with HIP events
+recorded on the forward's stream at its boundaries, in a pass of the same
+forwards right after the timed region; the CPU oracle is timed on a bounded
+sample on the host cores.
+
+The secondary measurements (weight quantization, cold-cache forwards, the
+dense linear, the skewed and W4A16 workloads, the masked layout, the router,
+decode sizes) run before the headline forwards.  They also bring the GPU
+from idle to its steady clocks, which takes about 80 back-to-back forwards,
+so the W warm-up steps and the K timed steps see the clocks of a layer that
+runs continuously, whatever W is.
 """
 from __future__ import annotations
 
@@ -38,7 +46,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--tokens", type=int, default=4096)
-    ap.add_argument("--cold-steps", type=int, default=10, help="extra forwards timed after a cache-evicting write")
+    ap.add_argument("--cold-steps", type=int, default=50, help="extra forwards timed after a cache-evicting write")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-sized (T = 1, 8, 64) forwards")
     ap.add_argument("--no-w4a16", action="store_true", help="skip the W4A16 variant's forwards")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense NVFP4 linear")
@@ -49,6 +57,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (reference dispatch for HBM byte counters)")
+    ap.add_argument("--oracle-single-thread", action="store_true", help=argparse.SUPPRESS)
     return ap.parse_args()
 
 
@@ -89,6 +98,39 @@ def fc1_traffic_bytes():
     return float(fields["fc1_traffic_bytes_per_launch"])
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_single_thread():
+    """Child process (OMP_NUM_THREADS=1, no GPU): the oracle on one thread, on
+    the tiny layer (64 tokens, whole) and the dense linear (the first 128 rows
+    of X [4096, 2048] against all of W [1536, 2048]).  Prints one JSON line."""
+    import oracle
+    import moe_workloads as W
+    tw = W.tiny(seed=0)
+    w1, w2 = tw.weights(threads=1)
+    wts = oracle.DequantWeights(w1, w2)
+    t0 = time.perf_counter()
+    oracle.moe_forward(tw.x, tw.ids, tw.probs, wts)
+    t_tiny = time.perf_counter() - t0
+    dw = W.dense(seed=1)
+    rows = 128
+    xq, wq = oracle.quantize(dw.x[:rows]), oracle.quantize(dw.w)
+    t0 = time.perf_counter()
+    oracle.linear(xq, wq)
+    t_dense = time.perf_counter() - t0
+    print(json.dumps({"tiny_layer_tokens_per_s": tw.shape.T / t_tiny, "tiny_layer_s": t_tiny,
+                      "dense_linear_gflop_per_s": 2.0 * rows * dw.N * dw.K / t_dense / 1e9, "dense_linear_s": t_dense,
+                      "dense_sample": f"first {rows} of {dw.M} rows of X x all {dw.N} rows of W"}))
+
+
 def cpu_baseline(wl, w1, w2, target_s):
     import oracle
     T = wl.shape.T
@@ -104,13 +146,27 @@ def cpu_baseline(wl, w1, w2, target_s):
     n = int(min(T, max(n0, n0 * target_s / max(t_small, 1e-3))))
     t = run(n) if n != n0 else t_small
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-    return {"value": n / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    single = None
+    try:
+        import subprocess
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-single-thread"], env=env,
+                           capture_output=True, text=True, timeout=300)
+        if r.returncode == 0:
+            single = json.loads(r.stdout.strip().splitlines()[-1])
+    except (OSError, ValueError, subprocess.SubprocessError):
+        single = None
+    return {"value": n / t, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"first {n} of {T} tokens of the same workload (all their top-{wl.shape.K} pairs), "
-                      f"weights pre-quantized and dequantized outside the timed region; {t:.1f} s"}
+                      f"weights pre-quantized and dequantized outside the timed region; {t:.1f} s",
+            "single_thread": single}
 
 
 def main():
     args = parse()
+    if args.oracle_single_thread:
+        oracle_single_thread()
+        return
     if args.gpus != 1:
         print(f"bench.py: the expert forward runs on one GPU; --gpus {args.gpus} is not supported "
               "(expert-parallel sharding across GPUs is not implemented)", file=sys.stderr)
@@ -144,36 +200,6 @@ def main():
         dst.copy_(src)  # reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        m.moe_expert_forward(cfg, x, ids, probs, qw, ws, out=out)
-    torch.cuda.synchronize()
-    if m.device_error(cfg, ws) != 0:
-        raise RuntimeError("device error word set")
-
-    # Timed region: exactly `steps` plain forwards, bracketed by device syncs.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        m.moe_expert_forward(cfg, x, ids, probs, qw, ws, out=out, stream=stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    # Stage breakdown in a separate pass (not part of `value`): the same forward
-    # with HIP events recorded on its stream at the stage boundaries.  Each
-    # event adds a few microseconds between kernels, so these forwards are a
-    # little slower than the timed ones; the kernels' own durations are not.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(m.N_STAGE_EVENTS)] for _ in range(args.steps)]
-    for ev in events:  # torch creates the underlying hipEvent on first record
-        for e in ev:
-            e.record(stream)
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        m.moe_expert_forward_events(cfg, x, ids, probs, qw, ws, events[k], out, stream=stream)
-    torch.cuda.synchronize()
-    stage_ms = np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(m.N_STAGE_EVENTS - 1)] for ev in events])
-    stage_mean = stage_ms.mean(axis=0)
-
     # Weight quantization (once per weight update, outside the forward): W1 and W2
     # re-quantized in place, timed with events on the stream.
     wq = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -193,6 +219,8 @@ def main():
     if args.cold_steps > 0:
         scratch = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(5):
+            m.moe_expert_forward(cfg, x, ids, probs, qw, ws, out=out)
         for _ in range(args.cold_steps):
             scratch.fill_(1)
             e0.record(stream)
@@ -349,6 +377,36 @@ def main():
                                "graph_us": ev[2].elapsed_time(ev[3]) / 200 * 1e3}
             del g
 
+    for _ in range(args.warmup):
+        m.moe_expert_forward(cfg, x, ids, probs, qw, ws, out=out)
+    torch.cuda.synchronize()
+    if m.device_error(cfg, ws) != 0:
+        raise RuntimeError("device error word set")
+
+    # Timed region: exactly `steps` plain forwards, bracketed by device syncs.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        m.moe_expert_forward(cfg, x, ids, probs, qw, ws, out=out, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # Stage breakdown in a separate pass (not part of `value`): the same forward
+    # with HIP events recorded on its stream at the stage boundaries.  Each
+    # event adds a few microseconds between kernels, so these forwards are a
+    # little slower than the timed ones; the kernels' own durations are not.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(m.N_STAGE_EVENTS)] for _ in range(args.steps)]
+    for ev in events:  # torch creates the underlying hipEvent on first record
+        for e in ev:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        m.moe_expert_forward_events(cfg, x, ids, probs, qw, ws, events[k], out, stream=stream)
+    torch.cuda.synchronize()
+    stage_ms = np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(m.N_STAGE_EVENTS - 1)] for ev in events])
+    stage_mean = stage_ms.mean(axis=0)
+
     P = T * K
     layer_flop = 2.0 * P * 3 * H * I
     fc1_flop = 2.0 * P * H * 2 * I
@@ -388,6 +446,8 @@ def main():
                   "stage_ms": dict(zip(m.STAGES, [round(float(v), 4) for v in stage_mean])),
                   "fc2_tflops": fc2_flop / (stage_mean[3] / 1e3) / 1e12,
                   "cold_ms_median": float(np.median(cold)) if cold else None,
+                  "cold_ms_p10_p90": [float(np.percentile(cold, 10)), float(np.percentile(cold, 90))] if cold else None,
+                  "cold_forwards": len(cold),
                   "cold_tokens_per_s": T / (np.median(cold) / 1e3) if cold else None},
         "weight_quantization": {"ms": wq_ms, "bytes": wq_bytes, "GB_s": wq_bytes / (wq_ms / 1e3) / 1e9,
                                 "frac_hbm_peak": wq_bytes / (wq_ms / 1e3) / 1e9 / HBM_PEAK_GBS,

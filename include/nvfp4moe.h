@@ -132,8 +132,12 @@ NVFP4MOE_API int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, i
 
 /* Bytes of one quantized expert-weight tensor: which = 1 for W1 [E, 2I, H]
  * (rows 0..I-1 of each expert are the gate projection, I..2I-1 the up
- * projection), which = 2 for W2 [E, H, I].  Sum of the three planes, each
- * rounded up to 256 bytes.  Returns 0 for an invalid config. */
+ * projection), which = 2 for W2 [E, H, I].  Sum of the three planes (E2M1
+ * codes, one E4M3 scale per 16 elements, one FP32 outer scale per row: the
+ * weight format of the miniTE page, "how it differs"), each rounded up to
+ * 256 bytes.  The caller allocates them once and the weights are re-quantized
+ * into the same buffers on every update (article, section 4.6: weights
+ * updated in place, addresses kept).  Returns 0 for an invalid config. */
 NVFP4MOE_API size_t nvfp4moe_weight_bytes(const nvfp4moe_config* cfg, int32_t which);
 
 /* Quantize BF16 expert weights (w1 [E, 2I, H], w2 [E, H, I]) in place into
@@ -144,7 +148,12 @@ NVFP4MOE_API int nvfp4moe_quantize_weights(const nvfp4moe_config* cfg, const uin
                               const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q, void* stream);
 
 /* Workspace bytes for the forward; depends on cfg only (max_tokens bounds T),
- * so one allocation serves every batch size.  Returns 0 for an invalid cfg. */
+ * so one allocation serves every batch size (article, section 4.6: buffers of
+ * static capacity sized once, no read-back of per-expert counts to size them;
+ * miniTE page, "how to use it": the quantizer writes and the GEMM reads one
+ * contiguous buffer).  It holds the sort metadata, the quantized sorted
+ * activations, h, the quantized h and the expert outputs
+ * (nvfp4moe_workspace_layout).  Returns 0 for an invalid cfg. */
 NVFP4MOE_API size_t nvfp4moe_workspace_bytes(const nvfp4moe_config* cfg);
 
 /* The NVFP4 MoE expert forward for T tokens.
@@ -161,6 +170,27 @@ NVFP4MOE_API size_t nvfp4moe_workspace_bytes(const nvfp4moe_config* cfg);
 NVFP4MOE_API int nvfp4moe_moe_expert_forward(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids,
                                 const float* probs, const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q,
                                 uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same forward with FC1 and the SwiGLU producer unfused, as a reference
+ * for the fused path (miniTE page, "assumptions and limits": the fused
+ * kernels are checked bit for bit against the unfused quantization and
+ * grouped-GEMM steps).  FC1 runs as a plain grouped GEMM whose epilogue
+ * writes y1 = bf16(acc * g^x * g^w1) for all 2I weight rows, then a separate
+ * kernel forms h = bf16(silu(gate) * up * p) and its per-32-column maxima
+ * from y1; every later step is the fused forward's.  Each value it writes
+ * (h, the maxima, A2, y2, out) has the fused forward's bits.
+ *   y1       [y1_rows, 2I] BF16, caller-owned (16-byte aligned); sorted row r
+ *            holds y1 of the pair in row r (columns 0..I-1 gate, I..2I-1 up);
+ *            padding rows are not written
+ *   y1_rows  >= rows_cap of nvfp4moe_workspace_layout (else NVFP4_E_SHAPE)
+ * Every other argument, the workspace and the errors are those of
+ * nvfp4moe_moe_expert_forward.  Slower than the fused forward (y1 makes a
+ * round trip through memory); meant for checking and inspection. */
+NVFP4MOE_API int nvfp4moe_moe_expert_forward_unfused(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T,
+                                                     const int32_t* ids, const float* probs, const nvfp4_qtensor* W1q,
+                                                     const nvfp4_qtensor* W2q, uint16_t* out, uint16_t* y1,
+                                                     int64_t y1_rows, void* workspace, size_t workspace_bytes,
+                                                     void* stream);
 
 /* The W4A16 variant of the expert forward (the article, section 6: NVFP4
  * W4A16 routed experts): the same sort, SwiGLU producer, combine, arguments,
@@ -191,7 +221,11 @@ NVFP4MOE_API int nvfp4moe_moe_expert_forward_events(const nvfp4moe_config* cfg, 
 /* Device error word of the last forward that used `workspace`: 0 if clean,
  * else a bitwise OR of 1 (an id outside [0, E)), 2 (an id repeated within a
  * token) and 4 (masked layout only: an expert received more pairs than its
- * capacity).  Syncs `stream`.  *code_host (host) receives the word. */
+ * capacity).  The routing (ids and probabilities) is an input decided
+ * upstream (article, section 4.4: the router's top-k is fixed before the
+ * expert path); the forward checks it on the device without a host read-back
+ * (section 4.6) and reports violations here instead of faulting.
+ * Syncs `stream`.  *code_host (host) receives the word. */
 NVFP4MOE_API int nvfp4moe_device_error(const nvfp4moe_config* cfg, const void* workspace, int32_t* code_host, void* stream);
 
 /* Byte offsets of the forward's intermediates inside the workspace, for
@@ -262,10 +296,17 @@ NVFP4MOE_API int nvfp4moe_router_topk(const uint16_t* x, int32_t T, int32_t H, c
                                       int32_t K, int32_t renormalize, float* logits, int32_t* ids, float* probs,
                                       void* stream);
 
-/* Dense NVFP4 linear: out [M, N] = bf16((Q(x) . Wq^T) * g^x * g^w), with
- * x [M, K] BF16 and Wq one GEMM-layout matrix [N, K] (n_mats 1).  The
- * activation quantization uses scale_round.  M >= 0, K % 128 == 0,
- * N % 128 == 0. */
+/* Dense NVFP4 linear (miniTE page, "how it differs": the NVFP4 linear with a
+ * per-token outer scale g^x and a per-weight-row g^w, whose FP32 epilogue
+ * multiplies the FP32 accumulator by g^x * g^w and casts to BF16; "how to
+ * use it": the quantizer's buffer is the GEMM's input):
+ *   out [M, N] = bf16((Q(x) . Wq^T) * g^x * g^w)
+ * with x [M, K] BF16 (16-byte aligned), Wq one GEMM-layout matrix [N, K]
+ * (n_mats 1), out [M, N] BF16 caller-owned.  Q(x) per row uses scale_round
+ * and goes to the workspace (nvfp4_linear_workspace_bytes(M, K) bytes,
+ * 256-byte aligned, caller-owned).  M >= 0, K % 128 == 0, N % 128 == 0; M = 0
+ * is a no-op.  Each output row depends on its own x row only (one K order,
+ * no split-K).  Errors as for the forward; no synchronisation. */
 NVFP4MOE_API size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K);
 NVFP4MOE_API int nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const nvfp4_qtensor* Wq, uint16_t* out,
                  int32_t scale_round, void* workspace, size_t workspace_bytes, void* stream);

@@ -26,7 +26,8 @@ EXPORTS = ["nvfp4_status_str", "nvfp4_quantize", "nvfp4moe_weight_bytes", "nvfp4
            "nvfp4moe_workspace_bytes", "nvfp4moe_moe_expert_forward", "nvfp4moe_moe_expert_forward_events",
            "nvfp4moe_device_error",
            "nvfp4moe_workspace_layout", "nvfp4moe_workspace_bytes_masked", "nvfp4moe_workspace_layout_masked",
-           "nvfp4moe_moe_expert_forward_masked", "nvfp4moe_moe_expert_forward_w4a16", "nvfp4moe_router_topk", "nvfp4_linear_workspace_bytes", "nvfp4_linear",
+           "nvfp4moe_moe_expert_forward_masked", "nvfp4moe_moe_expert_forward_unfused",
+           "nvfp4moe_moe_expert_forward_w4a16", "nvfp4moe_router_topk", "nvfp4_linear_workspace_bytes", "nvfp4_linear",
            "nvfp4moe_selftest_batch_invariance"]
 
 
@@ -82,6 +83,8 @@ def lib():
         "nvfp4moe_workspace_layout_masked": (ctypes.c_int, [cfgp, i32, ctypes.POINTER(WsLayout)]),
         "nvfp4moe_moe_expert_forward_masked": (ctypes.c_int, [cfgp, i32, vp, i32, vp, vp, qtp, qtp, vp, vp, sz, vp]),
         "nvfp4moe_moe_expert_forward_w4a16": (ctypes.c_int, [cfgp, vp, i32, vp, vp, qtp, qtp, vp, vp, sz, vp]),
+        "nvfp4moe_moe_expert_forward_unfused": (ctypes.c_int, [cfgp, vp, i32, vp, vp, qtp, qtp, vp, vp, i64, vp, sz,
+                                                                vp]),
         "nvfp4moe_router_topk": (ctypes.c_int, [vp, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp]),
         "nvfp4_linear_workspace_bytes": (sz, [i64, i64]),
         "nvfp4_linear": (ctypes.c_int, [vp, i64, i64, qtp, vp, i32, vp, sz, vp]),
@@ -229,6 +232,25 @@ def moe_expert_forward_w4a16(cfg: Config, x, ids, probs, weights: QuantWeights, 
     return out
 
 
+def moe_expert_forward_unfused(cfg: Config, x, ids, probs, weights: QuantWeights, workspace, y1=None, out=None,
+                               stream=None):
+    """nvfp4moe_moe_expert_forward_unfused: the forward with FC1 writing y1 [rows_cap, 2I] BF16 and the
+    SwiGLU producer as a separate kernel.  Returns (out, y1)."""
+    import torch
+    T = x.shape[0]
+    rows = workspace_layout(cfg).rows_cap
+    if out is None:
+        out = torch.empty((T, cfg.hidden), dtype=x.dtype, device=x.device)
+    if y1 is None:
+        y1 = torch.empty((rows, 2 * cfg.inter), dtype=x.dtype, device=x.device)
+    st = lib().nvfp4moe_moe_expert_forward_unfused(ctypes.byref(cfg), _ptr(x), T, _ptr(ids), _ptr(probs),
+                                                   ctypes.byref(weights.W1q), ctypes.byref(weights.W2q), _ptr(out),
+                                                   _ptr(y1), y1.shape[0], _ptr(workspace), workspace.numel(),
+                                                   _stream(stream))
+    _check(st, "nvfp4moe_moe_expert_forward_unfused")
+    return out, y1
+
+
 def moe_expert_forward(cfg: Config, x, ids, probs, weights: QuantWeights, workspace, out=None, stream=None):
     """nvfp4moe_moe_expert_forward: x [T,H] BF16, ids [T,K] int32, probs [T,K] float32 -> out [T,H] BF16."""
     import torch
@@ -273,6 +295,11 @@ def router_topk(x, w_router, k: int, renormalize: bool = True, stream=None, out=
     E = w_router.shape[0]
     if out is not None:
         logits, ids, probs = out
+        for t, name, shape, dtype in ((logits, "logits", (T, E), torch.float32), (ids, "ids", (T, k), torch.int32),
+                                      (probs, "probs", (T, k), torch.float32)):
+            if tuple(t.shape) != shape or t.dtype != dtype or not t.is_contiguous() or t.device != x.device:
+                raise ValueError(f"router_topk: out {name} must be a contiguous {dtype} tensor of shape {shape} "
+                                 f"on {x.device}, got {tuple(t.shape)} {t.dtype} on {t.device}")
     else:
         logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
         ids = torch.empty((T, k), dtype=torch.int32, device=x.device)

@@ -217,10 +217,12 @@ namespace {
 // at each stage boundary (before the sort, after the sort, after FC1, after
 // the FC2-input quantizer, after FC2, after the combine).
 // capacity 0: the contiguous row layout; > 0: the masked layout.
+// y1 non-null: the unfused forward -- FC1 as a plain grouped GEMM writing
+// y1 [rows_cap, 2I], then the SwiGLU producer as a kernel of its own.
 int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids, const float* probs,
                  const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q, uint16_t* out, void* workspace,
                  size_t workspace_bytes, void* stream, void* const* events, int32_t capacity = 0,
-                 bool w4a16 = false) {
+                 bool w4a16 = false, uint16_t* y1 = nullptr) {
     if (!cfg) return NVFP4_E_NULL;
     if (!cfg_ok(cfg)) return NVFP4_E_SHAPE;
     if (capacity != 0 && !capacity_ok(cfg, capacity)) return NVFP4_E_SHAPE;
@@ -328,16 +330,33 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     f1.amax_part = (float*)(ws + L.pub.amax2_part);
     f1.n_part = (int32_t)(I / 32);
     f1.inter = (int32_t)I;
-    // FC1: hybrid grid -- two workgroups per CU walk a static bulk of equal
-    // tile counts, and the last one to two rounds of tiles go one per
-    // workgroup to the rest of the grid, which the hardware dispatcher hands
-    // to whichever CU slot frees first.  Measured on the Qwen3-30B-A3B-shaped
-    // layer at T = 4096: about 8 us faster than persistent workgroups alone
-    // and 2-3 us faster than one workgroup per tile; FC2's shorter tiles
-    // (K = I) are fastest persistent.
-    f1.persist = hybrid_persist();
-    e = launch_gemm(kGemmSwiGLU, f1, hybrid_grid(mt_bound * f1.n_tiles_n), s);
-    if (e != hipSuccess || !mark(2)) return NVFP4_E_HIP;
+    if (y1) {
+        // Unfused: y1 = bf16(acc * g^x * g^w1) for all 2I weight rows (the
+        // plain epilogue, whose arithmetic per element is the fused one's),
+        // then h and its maxima from y1 in a separate kernel.
+        GemmParams u = f1;
+        u.N = (int32_t)(2 * I);
+        u.n_tiles_n = col_tiles(2 * I, kGemmPlain);
+        u.out = y1;
+        u.ld_out = 2 * I;
+        e = launch_gemm(kGemmPlain, u, grid_blocks(mt_bound * u.n_tiles_n), s);
+        if (e != hipSuccess) return NVFP4_E_HIP;
+        const int64_t rb1 = std::min<int64_t>(L.pub.rows_cap, mt_bound * kTileRows);
+        e = launch_swiglu_producer(y1, rb1, (int32_t)I, rb.row2pair, rb.row_prob, rb.expert_off, (int32_t)E, f1.out,
+                                   f1.amax_part, s);
+        if (e != hipSuccess || !mark(2)) return NVFP4_E_HIP;
+    } else {
+        // FC1: hybrid grid -- two workgroups per CU walk a static bulk of
+        // equal tile counts, and the last one to two rounds of tiles go one
+        // per workgroup to the rest of the grid, which the hardware
+        // dispatcher hands to whichever CU slot frees first.  Measured on the
+        // Qwen3-30B-A3B-shaped layer at T = 4096: about 8 us faster than
+        // persistent workgroups alone and 2-3 us faster than one workgroup
+        // per tile; FC2's shorter tiles (K = I) are fastest persistent.
+        f1.persist = hybrid_persist();
+        e = launch_gemm(kGemmSwiGLU, f1, hybrid_grid(mt_bound * f1.n_tiles_n), s);
+        if (e != hipSuccess || !mark(2)) return NVFP4_E_HIP;
+    }
 
     uint8_t* a2c = ws + L.pub.a2_codes;
     uint8_t* a2s = ws + L.pub.a2_scales;
@@ -398,6 +417,19 @@ int nvfp4moe_moe_expert_forward_masked(const nvfp4moe_config* cfg, int32_t capac
                                        size_t workspace_bytes, void* stream) {
     if (cfg && cfg_ok(cfg) && !capacity_ok(cfg, capacity)) return NVFP4_E_SHAPE;
     return forward_impl(cfg, x, T, ids, probs, W1q, W2q, out, workspace, workspace_bytes, stream, nullptr, capacity);
+}
+
+int nvfp4moe_moe_expert_forward_unfused(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids,
+                                        const float* probs, const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q,
+                                        uint16_t* out, uint16_t* y1, int64_t y1_rows, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+    if (!cfg) return NVFP4_E_NULL;
+    if (!cfg_ok(cfg)) return NVFP4_E_SHAPE;
+    if (y1_rows < make_layout(cfg).pub.rows_cap) return NVFP4_E_SHAPE;
+    if (T > 0 && !y1) return NVFP4_E_NULL;
+    if (y1 && !aligned(y1, 16)) return NVFP4_E_ALIGN;
+    return forward_impl(cfg, x, T, ids, probs, W1q, W2q, out, workspace, workspace_bytes, stream, nullptr, 0, false,
+                        T > 0 ? y1 : nullptr);
 }
 
 int nvfp4moe_moe_expert_forward_w4a16(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids,

@@ -69,15 +69,6 @@ __device__ __forceinline__ void scales_of(uint32_t sdw, half2v& lo, half2v& hi) 
     hi = scale2<2 * CH + 1>(sdw);
 }
 
-// float -> BF16 bits with the hardware conversion (round to nearest even).
-__device__ __forceinline__ uint32_t bf16_hw(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
-
-// silu(a) = a / (1 + e^-a), with the hardware exp2 and reciprocal.
-__device__ __forceinline__ float silu_fast(float a) {
-    const float e = __builtin_amdgcn_exp2f(a * -1.4426950408889634f);
-    return a * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 
@@ -351,7 +342,7 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
                 const float pr = P.row_prob[row];
                 const float yg = bf16_to_f32(bf16_hw(acc[i][0][r] * (gx * cg[0])));
                 const float yu = bf16_to_f32(bf16_hw(acc[i][1][r] * (gx * cg[1])));
-                E[rl * kPitch + colL] = (uint16_t)bf16_hw(silu_fast(yg) * yu * pr);
+                E[rl * kPitch + colL] = (uint16_t)swiglu_prob_bf16(yg, yu, pr);
             }
         }
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);

@@ -48,11 +48,6 @@ __device__ __forceinline__ float w16_scale(uint32_t sw, int sel) {
     }
 }
 
-__device__ __forceinline__ uint32_t w16_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
-__device__ __forceinline__ float w16_silu(float a) {
-    const float e = __builtin_amdgcn_exp2f(a * -1.4426950408889634f);
-    return a * __builtin_amdgcn_rcpf(1.0f + e);
-}
 
 // Workgroup barrier ordering LDS accesses only: global loads in flight (the
 // next step's weights) stay in flight; the compiler waits for loaded values
@@ -195,9 +190,9 @@ __device__ __forceinline__ void w16_tile(const W16Params& P, W16SharedA& S, int3
             for (int i = 0; i < 16; i++) {
                 const int rr = (i >> 2) * 8 + rowL + (i & 3);
                 const int32_t row = min(row0 + 32 * t + rr, row_end - 1);  // rows past the end are not stored
-                const float yg = __uint_as_float(w16_bf16_rne(acc[t][0][i] * gg) << 16);
-                const float yu = __uint_as_float(w16_bf16_rne(acc[t][1][i] * gu) << 16);
-                E[rr * kPitch + r] = (uint16_t)w16_bf16_rne(w16_silu(yg) * yu * P.row_prob[row]);
+                const float yg = __uint_as_float(bf16_hw(acc[t][0][i] * gg) << 16);
+                const float yu = __uint_as_float(bf16_hw(acc[t][1][i] * gu) << 16);
+                E[rr * kPitch + r] = (uint16_t)swiglu_prob_bf16(yg, yu, P.row_prob[row]);
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slice is written
             __builtin_amdgcn_wave_barrier();
@@ -219,8 +214,8 @@ __device__ __forceinline__ void w16_tile(const W16Params& P, W16SharedA& S, int3
 #pragma unroll
             for (int i = 0; i < 16; i++) {
                 const int rr = (i >> 2) * 8 + rowL + (i & 3);
-                E[rr * kPitch + r] = (uint16_t)w16_bf16_rne(acc[t][0][i] * g0);
-                E[rr * kPitch + 32 + r] = (uint16_t)w16_bf16_rne(acc[t][1][i] * g1);
+                E[rr * kPitch + r] = (uint16_t)bf16_hw(acc[t][0][i] * g0);
+                E[rr * kPitch + 32 + r] = (uint16_t)bf16_hw(acc[t][1][i] * g1);
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);
             __builtin_amdgcn_wave_barrier();

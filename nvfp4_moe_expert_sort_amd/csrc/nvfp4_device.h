@@ -31,6 +31,23 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// float -> BF16 bits with the hardware conversion (round to nearest even).
+__device__ __forceinline__ uint32_t bf16_hw(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// silu(a) = a / (1 + e^-a) in FP32 with the hardware base-2 exponential
+// (v_exp_f32, on a * -log2(e)) and reciprocal (v_rcp_f32).  Used by the FC1
+// epilogue and by the separate SwiGLU producer, so both give the same bits.
+__device__ __forceinline__ float silu_fast(float a) {
+    const float e = __builtin_amdgcn_exp2f(a * -1.4426950408889634f);
+    return a * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// The router-weighted SwiGLU output of one element: gate and up are the BF16
+// FC1 outputs (as FP32), p the router probability; one BF16 rounding.
+__device__ __forceinline__ uint32_t swiglu_prob_bf16(float gate, float up, float p) {
+    return bf16_hw(silu_fast(gate) * up * p);
+}
+
 // E4M3FN byte of a non-negative block scale v.  round_up: the smallest E4M3FN
 // value >= v; otherwise nearest with ties to an even mantissa.  Clamped to
 // 448 (0x7E); 0 for v <= 0.  The hardware conversion v_cvt_pk_fp8_f32 rounds

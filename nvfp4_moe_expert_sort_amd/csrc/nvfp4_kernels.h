@@ -111,6 +111,12 @@ __device__ __forceinline__ bool row_tile_used(int64_t rt, int32_t E, int32_t cap
 #endif
 int gemm_cols_per_tile(int mode);  // output columns per tile: 256 (plain) or 128 of h (128 gate + 128 up rows)
 hipError_t launch_gemm(int mode, const GemmParams& P, int grid_blocks, hipStream_t stream);
+// The router-weighted SwiGLU producer on its own (unfused forward): h and the
+// per-32-column maxima of |h| from y1 [rows, 2I] (gate | up), for sorted rows
+// below min(rows_bound, expert_off[E]) that hold a pair.
+hipError_t launch_swiglu_producer(const uint16_t* y1, int64_t rows_bound, int32_t I, const int32_t* row2pair,
+                                  const float* row_prob, const int32_t* expert_off, int32_t E, uint16_t* h,
+                                  float* amax_part, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* y2, const int32_t* pair2row, int32_t T, int32_t H, int32_t K,
                           uint16_t* out, hipStream_t stream);
 

@@ -13,12 +13,17 @@ Per workload and capacity, through the C ABI:
     outputs are equal;
   - an expert with more pairs than the capacity: error bit 4, the pairs past
     the capacity get no row, and every token none of whose pairs was dropped
-    keeps its contiguous-layout output bits."""
+    keeps its contiguous-layout output bits;
+  - against the oracle: the masked sort metadata (offsets, pair -> row,
+    row -> pair inside each expert's used rows, dropped pairs) bit-exact with
+    the oracle's masked layout, and every stage of the masked forward
+    element-wise against the oracle (tests/layer_parity.py)."""
 import numpy as np
 import pytest
 
 import moe_workloads as W
 from tests.helpers import to_dev, to_host
+from tests.layer_parity import check_route, parity
 
 pytestmark = pytest.mark.gpu
 
@@ -79,6 +84,7 @@ def _both(m, dev, wl, capacity, mode=0):
     torch.cuda.synchronize()
     cont = Run(m, cfg, m.workspace_layout(cfg), ws_c, out_c, s)
     mask = Run(m, cfg, m.workspace_layout_masked(cfg, capacity), ws_m, out_m, s)
+    mask.weights = (w1, w2)
     return cont, mask
 
 
@@ -107,7 +113,7 @@ def _check_placement(cont, mask, pairs, capacity, ids):
 
 
 @pytest.mark.parametrize("case", ["tiny-RU", "tiny-RNE", "qwen3", "skewed"])
-def test_masked_rows_equal_contiguous_rows(gpu, case):
+def test_masked_rows_equal_contiguous_rows(gpu, orc, case):
     m, dev = gpu
     wl, capacity, mode = {"tiny-RU": (W.tiny(seed=0), 32, 0), "tiny-RNE": (W.tiny(seed=0), 64, 1),
                           "qwen3": (W.qwen3(seed=2, T=4096), 320, 0),
@@ -126,15 +132,22 @@ def test_masked_rows_equal_contiguous_rows(gpu, case):
         assert np.all(mask.r2p[e * capacity + n:e * capacity + pad] == -1), f"padding rows of expert {e}"
     assert np.array_equal(mask.out, cont.out), "outputs differ between the layouts"
     print(f"  {case}: capacity {capacity}, {s.T * s.K} pairs, every row and output bit-equal")
+    # the masked forward against the oracle: metadata bit-exact, every stage element-wise
+    lay_m = m.workspace_layout_masked(m.make_config(s.H, s.I, s.E, s.K, s.T, scale_round=mode), capacity)
+    parity(orc, s, lay_m, mask.ws, wl.x, wl.ids, wl.probs, mask.out, *mask.weights, mode=mode, capacity=capacity,
+           label=f"masked {case}")
 
 
-def test_masked_capacity_overflow(gpu):
+def test_masked_capacity_overflow(gpu, orc):
     m, dev = gpu
     wl = W.qwen3(seed=2, T=4096)  # 213..298 pairs per expert
     capacity = 256
     s = wl.shape
     cont, mask = _both(m, dev, wl, capacity)
     assert cont.err == 0 and mask.err == 4, f"error word {mask.err}"
+    # metadata against the oracle's masked layout, dropped pairs included
+    check_route(orc, s.E, s.K, s.T, m.workspace_layout_masked(m.make_config(s.H, s.I, s.E, s.K, s.T), capacity),
+                mask.ws, wl.ids, capacity)
     e = wl.ids.reshape(-1)
     rank = cont.p2r - cont.off[e]
     dropped = rank >= capacity

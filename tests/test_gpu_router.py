@@ -66,10 +66,15 @@ def test_router_parity(gpu, case, renorm):
     print(f"  {case} renorm={renorm}: T={s.T} E={s.E} K={s.K}, max score error {e_l:.3g}, max prob rel {e_p:.3g}")
 
 
-@pytest.mark.parametrize("T,H,E,K", [(33, 144, 50, 7), (5, 2048, 1024, 32), (70, 64, 3, 3)])
+@pytest.mark.parametrize("T,H,E,K", [(33, 144, 50, 7), (5, 2048, 1024, 32), (70, 64, 3, 3),
+                                     (33, 144, 200, 8), (70, 256, 256, 8), (5, 144, 257, 8),
+                                     (40, 128, 129, 8), (9, 128, 255, 32)])
 def test_router_ragged_shapes(gpu, T, H, E, K):
     """Expert counts that are not multiples of 32 or 64, the largest E and K, a
-    token count with a partial 32-token tile, H not a multiple of 64."""
+    token count with a partial 32-token tile, H not a multiple of 64; both
+    top-k paths: rank counting (E <= 256, including 129..256 with four keys per
+    lane and the E = 256 edge) and the rounds of wave-wide maxima (E = 257 and
+    1024)."""
     m, dev = gpu
     rng = np.random.default_rng(E)
     x = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
@@ -94,9 +99,28 @@ def test_router_batch_invariance(gpu):
                                   (b[rows].view(np.uint32) if b.dtype == np.float32 else b[rows])), f"{name}, T={T}"
 
 
-def test_router_ties_go_to_the_lower_id(gpu):
+def test_router_out_buffers_are_checked(gpu):
+    """Caller-provided output tensors of the wrong shape, dtype or layout raise
+    before the kernel is launched."""
+    import torch
     m, dev = gpu
-    E, H, K = 64, 256, 6
+    T, H, E, K = 8, 128, 16, 4
+    x = to_dev(W.f32_to_bf16_bits(np.ones((T, H), np.float32)), dev)
+    w = to_dev(_router_weights(E, H, 25), dev)
+    good = (torch.empty((T, E), dtype=torch.float32, device=dev), torch.empty((T, K), dtype=torch.int32, device=dev),
+            torch.empty((T, K), dtype=torch.float32, device=dev))
+    m.router_topk(x, w, K, out=good)
+    for bad in ((good[0][:, :E - 1], good[1], good[2]), (good[0], good[1].float(), good[2]),
+                (good[0], good[1], torch.empty((K, T), dtype=torch.float32, device=dev).t()),
+                (good[0].cpu(), good[1], good[2])):
+        with pytest.raises(ValueError):
+            m.router_topk(x, w, K, out=bad)
+
+
+@pytest.mark.parametrize("E", [64, 256])
+def test_router_ties_go_to_the_lower_id(gpu, E):
+    m, dev = gpu
+    H, K = 256, 6
     w = _router_weights(E, H, 23)
     w[9] = w[5]      # experts 5 and 9 always score the same
     w[40] = w[12]    # and 12 and 40

@@ -13,7 +13,13 @@ separate launch per step:
   FC2       nvfp4_linear per expert on that expert's rows of h with the
             expert's W2.
 It must reproduce the fused forward's A1 (sorted, padded, quantized X), A2
-(quantized h, whose amax came from the SwiGLU producer) and y2 bit for bit."""
+(quantized h, whose amax came from the SwiGLU producer) and y2 bit for bit.
+
+FC1 and the producer: the library's unfused forward runs FC1 as a plain
+grouped GEMM writing y1 (both halves, gate and up) and then the router-
+weighted SwiGLU producer as a kernel of its own; its h, the per-32-column
+maxima of |h|, A2, y2 and the output must be the fused forward's bit for bit
+(the fused FC1 epilogue forms the same y1 values in registers)."""
 import numpy as np
 import pytest
 
@@ -103,3 +109,52 @@ def test_fused_equals_unfused_qwen3(gpu):
 def test_fused_equals_unfused_skewed(gpu):
     m, dev = gpu
     _fused_vs_unfused(m, dev, W.skewed(seed=3), 0)
+
+
+def _fused_vs_unfused_fc1(m, dev, wl, mode):
+    import torch
+    s = wl.shape
+    w1, w2 = wl.weights(threads=16)
+    cfg = m.make_config(s.H, s.I, s.E, s.K, s.T, scale_round=mode)
+    qw = m.QuantWeights(cfg, dev).quantize_from(to_dev(w1, dev), to_dev(w2, dev))
+    lay = m.workspace_layout(cfg)
+    x, ids, probs = to_dev(wl.x, dev), to_dev(wl.ids, dev), to_dev(wl.probs, dev)
+    ws_f, ws_u = m.alloc_workspace(cfg, dev), m.alloc_workspace(cfg, dev)
+    out_f = m.moe_expert_forward(cfg, x, ids, probs, qw, ws_f)
+    out_u, y1 = m.moe_expert_forward_unfused(cfg, x, ids, probs, qw, ws_u)
+    torch.cuda.synchronize()
+    assert m.device_error(cfg, ws_f) == 0 and m.device_error(cfg, ws_u) == 0
+
+    def view(ws, off, dtype, count):
+        return ws[off:off + count * torch.tensor([], dtype=dtype).element_size()].view(dtype)
+
+    rows = int(to_host(view(ws_f, lay.expert_off, torch.int32, s.E + 1))[-1])
+    valid = view(ws_f, lay.row2pair, torch.int32, rows) >= 0
+    for name, n in (("h", s.I), ("y2", s.H)):
+        a = view(ws_f, getattr(lay, name), torch.int16, rows * n).view(rows, n)[valid]
+        b = view(ws_u, getattr(lay, name), torch.int16, rows * n).view(rows, n)[valid]
+        assert torch.equal(a, b), name
+    a = view(ws_f, lay.amax2_part, torch.int32, rows * lay.n_part).view(rows, lay.n_part)[valid]
+    b = view(ws_u, lay.amax2_part, torch.int32, rows * lay.n_part).view(rows, lay.n_part)[valid]
+    assert torch.equal(a, b), "FC2 maxima from the producer"
+    for name, n in (("a2_codes", s.I // 2), ("a2_scales", s.I // 16), ("a2_g", 4)):
+        assert torch.equal(view(ws_f, getattr(lay, name), torch.uint8, rows * n),
+                           view(ws_u, getattr(lay, name), torch.uint8, rows * n)), name
+    assert torch.equal(out_f, out_u), "outputs"
+    print(f"  fused FC1 + producer == unfused over {int(valid.sum())} rows: h, maxima, A2, y2, out")
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_fused_fc1_producer_equals_unfused_tiny(gpu, mode):
+    m, dev = gpu
+    _fused_vs_unfused_fc1(m, dev, W.tiny(seed=0), mode)
+
+
+def test_fused_fc1_producer_equals_unfused_qwen3(gpu):
+    m, dev = gpu
+    _fused_vs_unfused_fc1(m, dev, W.qwen3(seed=2, T=4096), 0)
+
+
+def test_fused_fc1_producer_equals_unfused_skewed(gpu):
+    m, dev = gpu
+    _fused_vs_unfused_fc1(m, dev, W.skewed(seed=3), 0)
