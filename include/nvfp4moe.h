@@ -60,7 +60,8 @@ enum {
     NVFP4_E_HIP = 6,       /* a HIP launch or runtime call failed */
     NVFP4_E_MISMATCH = 7,  /* self-test found differing bits */
     NVFP4_E_DEVICE = 8,    /* the device reported a contract violation (see nvfp4moe_device_error) */
-    NVFP4_E_ARG = 9        /* an enum argument is out of range */
+    NVFP4_E_ARG = 9,       /* an enum argument is out of range */
+    NVFP4_E_SCRATCH = 10   /* the allocation-free forward's input exceeds its static scratch */
 };
 
 /* Rounding of the E4M3 block scale v = amax_block / (6 g).  The pages fix the
@@ -227,6 +228,31 @@ NVFP4MOE_API int nvfp4moe_moe_expert_forward_events(const nvfp4moe_config* cfg, 
  * (section 4.6) and reports violations here instead of faulting.
  * Syncs `stream`.  *code_host (host) receives the word. */
 NVFP4MOE_API int nvfp4moe_device_error(const nvfp4moe_config* cfg, const void* workspace, int32_t* code_host, void* stream);
+
+/* The forward with no workspace argument and no allocation, for callers that
+ * cannot allocate device memory on the way: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Its intermediates
+ * live in one static device array of NVFP4MOE_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the library's load until the process ends; its address is
+ * looked up once per device on the first call there.  Arguments and results
+ * are those of nvfp4moe_moe_expert_forward (same kernels, same bits), and:
+ *   err_word  optional (may be NULL) device int32: receives the call's
+ *             device error word (see nvfp4moe_device_error) by a 4-byte
+ *             device-to-device copy at the end of the call
+ * The intermediates need size nvfp4moe_workspace_bytes of cfg with
+ * max_tokens = T; a call whose T needs more than the scratch returns
+ * NVFP4_E_SCRATCH before any launch (at the Qwen3-30B-A3B layer shape,
+ * H 2048, I 768, E 128, K 8, that is T above about 600 tokens).  T above
+ * cfg->max_tokens returns NVFP4_E_CAPACITY.  Nothing in the scratch needs
+ * clearing between calls: every call writes what it reads.  All calls on one
+ * GPU share its scratch: calls that overlap in time on one GPU (different
+ * streams, or host threads) race and their results are undefined; serialise
+ * them (one stream, or events). */
+#define NVFP4MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+NVFP4MOE_API int nvfp4moe_moe_expert_forward_noalloc(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T,
+                                                     const int32_t* ids, const float* probs, const nvfp4_qtensor* W1q,
+                                                     const nvfp4_qtensor* W2q, uint16_t* out, int32_t* err_word,
+                                                     void* stream);
 
 /* Byte offsets of the forward's intermediates inside the workspace, for
  * inspection (host struct).  Row-indexed buffers are indexed by sorted row r

@@ -15,7 +15,9 @@ LIB_PATH = os.path.join(HERE, "lib", "libnvfp4moe.so")
 
 NVFP4_OK = 0
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_E_NULL", 2: "NVFP4_E_SHAPE", 3: "NVFP4_E_ALIGN", 4: "NVFP4_E_WORKSPACE",
-          5: "NVFP4_E_CAPACITY", 6: "NVFP4_E_HIP", 7: "NVFP4_E_MISMATCH", 8: "NVFP4_E_DEVICE", 9: "NVFP4_E_ARG"}
+          5: "NVFP4_E_CAPACITY", 6: "NVFP4_E_HIP", 7: "NVFP4_E_MISMATCH", 8: "NVFP4_E_DEVICE", 9: "NVFP4_E_ARG",
+          10: "NVFP4_E_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20
 SCALE_RU = 0
 SCALE_RNE = 1
 LAYOUT_LOGICAL = 0
@@ -27,6 +29,7 @@ EXPORTS = ["nvfp4_status_str", "nvfp4_quantize", "nvfp4moe_weight_bytes", "nvfp4
            "nvfp4moe_device_error",
            "nvfp4moe_workspace_layout", "nvfp4moe_workspace_bytes_masked", "nvfp4moe_workspace_layout_masked",
            "nvfp4moe_moe_expert_forward_masked", "nvfp4moe_moe_expert_forward_unfused",
+           "nvfp4moe_moe_expert_forward_noalloc",
            "nvfp4moe_moe_expert_forward_w4a16", "nvfp4moe_router_topk", "nvfp4_linear_workspace_bytes", "nvfp4_linear",
            "nvfp4moe_selftest_batch_invariance"]
 
@@ -83,6 +86,7 @@ def lib():
         "nvfp4moe_workspace_layout_masked": (ctypes.c_int, [cfgp, i32, ctypes.POINTER(WsLayout)]),
         "nvfp4moe_moe_expert_forward_masked": (ctypes.c_int, [cfgp, i32, vp, i32, vp, vp, qtp, qtp, vp, vp, sz, vp]),
         "nvfp4moe_moe_expert_forward_w4a16": (ctypes.c_int, [cfgp, vp, i32, vp, vp, qtp, qtp, vp, vp, sz, vp]),
+        "nvfp4moe_moe_expert_forward_noalloc": (ctypes.c_int, [cfgp, vp, i32, vp, vp, qtp, qtp, vp, vp, vp]),
         "nvfp4moe_moe_expert_forward_unfused": (ctypes.c_int, [cfgp, vp, i32, vp, vp, qtp, qtp, vp, vp, i64, vp, sz,
                                                                 vp]),
         "nvfp4moe_router_topk": (ctypes.c_int, [vp, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp]),
@@ -229,6 +233,22 @@ def moe_expert_forward_w4a16(cfg: Config, x, ids, probs, weights: QuantWeights, 
                                                  ctypes.byref(weights.W1q), ctypes.byref(weights.W2q), _ptr(out),
                                                  _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "nvfp4moe_moe_expert_forward_w4a16")
+    return out
+
+
+def moe_expert_forward_noalloc(cfg: Config, x, ids, probs, weights: QuantWeights, out=None, err_word=None,
+                               stream=None):
+    """nvfp4moe_moe_expert_forward_noalloc: as moe_expert_forward, with the intermediates in the library's
+    static per-GPU scratch (no workspace, no allocation by the library; `out` and `err_word`, a device
+    int32 that receives the device error word, may be given preallocated)."""
+    import torch
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, cfg.hidden), dtype=x.dtype, device=x.device)
+    st = lib().nvfp4moe_moe_expert_forward_noalloc(ctypes.byref(cfg), _ptr(x), T, _ptr(ids), _ptr(probs),
+                                                   ctypes.byref(weights.W1q), ctypes.byref(weights.W2q), _ptr(out),
+                                                   _ptr(err_word), _stream(stream))
+    _check(st, "nvfp4moe_moe_expert_forward_noalloc")
     return out
 
 

@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/nvfp4moe.h"
@@ -130,6 +131,37 @@ int32_t col_tiles(int64_t n, int mode) {
 
 }  // namespace
 
+// Scratch of the allocation-free forward: one static array per GPU the
+// library runs on.  Host code never passes `scratch` itself to a kernel or a
+// copy (on the host it names a stand-in, not device memory): it uses the
+// device address hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kNoAllocScratchBytes = NVFP4MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on its first use
+// there, with that device current).
+int noalloc_scratch(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return NVFP4_E_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return NVFP4_E_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NVFP4_E_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return NVFP4_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* nvfp4_status_str(int s) {
@@ -144,6 +176,7 @@ const char* nvfp4_status_str(int s) {
         case NVFP4_E_MISMATCH: return "batch-invariance mismatch";
         case NVFP4_E_DEVICE: return "device-side contract violation";
         case NVFP4_E_ARG: return "invalid enum argument";
+        case NVFP4_E_SCRATCH: return "token count too large for the allocation-free forward's static scratch";
         default: return "unknown status";
     }
 }
@@ -417,6 +450,28 @@ int nvfp4moe_moe_expert_forward_masked(const nvfp4moe_config* cfg, int32_t capac
                                        size_t workspace_bytes, void* stream) {
     if (cfg && cfg_ok(cfg) && !capacity_ok(cfg, capacity)) return NVFP4_E_SHAPE;
     return forward_impl(cfg, x, T, ids, probs, W1q, W2q, out, workspace, workspace_bytes, stream, nullptr, capacity);
+}
+
+int nvfp4moe_moe_expert_forward_noalloc(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids,
+                                        const float* probs, const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q,
+                                        uint16_t* out, int32_t* err_word, void* stream) {
+    if (!cfg) return NVFP4_E_NULL;
+    if (!cfg_ok(cfg)) return NVFP4_E_SHAPE;
+    if (T < 0) return NVFP4_E_SHAPE;
+    if (T > cfg->max_tokens) return NVFP4_E_CAPACITY;
+    if (err_word && !aligned(err_word, 4)) return NVFP4_E_ALIGN;
+    nvfp4moe_config c = *cfg;
+    c.max_tokens = T;  // the intermediates of exactly this call
+    const Layout L = make_layout(&c);
+    if (L.total > kNoAllocScratchBytes) return NVFP4_E_SCRATCH;
+    if (T == 0) return NVFP4_OK;
+    void* ws = nullptr;
+    const int st = noalloc_scratch(&ws);
+    if (st != NVFP4_OK) return st;
+    const int r = forward_impl(&c, x, T, ids, probs, W1q, W2q, out, ws, kNoAllocScratchBytes, stream, nullptr);
+    if (r != NVFP4_OK || !err_word) return r;
+    return hip_status(hipMemcpyAsync(err_word, (const uint8_t*)ws + L.pub.err, 4, hipMemcpyDeviceToDevice,
+                                     (hipStream_t)stream));
 }
 
 int nvfp4moe_moe_expert_forward_unfused(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids,
