@@ -79,6 +79,24 @@ __device__ __forceinline__ size_t gemm_scale_off(int64_t r, int64_t k, int64_t c
     return (size_t)((rt * (cols >> 7) + (c >> 1)) * 256 + (h * 32 + rl) * 4 + (c & 1) * 2 + ((k & 31) >> 4));
 }
 
+// --- XCD-aware block order ---------------------------------------------------------------------
+// A 1-D grid over (row-tile quad q, column group j) with j fastest within an
+// XCD: workgroups are dispatched round-robin over the 8 XCDs (block b runs on
+// XCD b % 8), so block b takes item b / 8 of XCD b % 8's list, whose items
+// are its quads x, x + 8, x + 16, ... each followed by all its column groups.
+// The column groups of one row-tile quad then run together on one XCD and
+// share its L2 for the per-row data they all read.  Returns false for the
+// padding blocks past the last quad.
+__device__ __forceinline__ bool xcd_quad_group(int64_t n_quads, int64_t groups, int64_t& quad, int64_t& group) {
+    const int64_t b = blockIdx.x, x = b & 7, i = b >> 3;
+    quad = (i / groups) * 8 + x;
+    group = i % groups;
+    return quad < n_quads;
+}
+inline unsigned xcd_quad_group_blocks(int64_t n_quads, int64_t groups) {
+    return (unsigned)(((n_quads + 7) / 8) * 8 * groups);
+}
+
 // --- wave reductions ----------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

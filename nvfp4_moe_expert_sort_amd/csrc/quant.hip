@@ -61,12 +61,16 @@ __global__ void __launch_bounds__(256) quant_h_kernel(const uint16_t* __restrict
                                                       int64_t n_row_tiles, uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ scales, float* __restrict__ g,
                                                       int round_up) {
-    // Grid: x covers 32-row tiles (four per block, one per wave), y the
-    // column groups of kQuantHSteps 128-column steps.
+    // Block: four 32-row tiles (one per wave) x one column group of
+    // kQuantHSteps 128-column steps; the groups of a quad run together on one
+    // XCD (xcd_quad_group), so its rows' maxima and pairs are fetched once.
     const int lane = threadIdx.x & 63;
-    const int64_t rt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t cps = I / 128;
+    int64_t quad, grp;
+    if (!xcd_quad_group((n_row_tiles + 3) / 4, (cps + kQuantHSteps - 1) / kQuantHSteps, quad, grp)) return;
+    const int64_t rt = quad * 4 + (threadIdx.x >> 6);
     if (rt >= n_row_tiles) return;
-    const int64_t cps = I / 128, cp0 = (int64_t)blockIdx.y * kQuantHSteps;
+    const int64_t cp0 = grp * kQuantHSteps;
     const int hh = lane >> 5, rl = lane & 31;
     const int64_t row = rt * 32 + rl;
     // Every load is issued before the test of whether this row tile holds an
@@ -142,7 +146,7 @@ hipError_t launch_quant_h(const uint16_t* h, int64_t rows_bound, int64_t I, cons
                           bool round_up, hipStream_t stream) {
     const int64_t n_row_tiles = rows_bound / 32, groups = (I / 128 + kQuantHSteps - 1) / kQuantHSteps;
     if (n_row_tiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_h_kernel, dim3((unsigned)((n_row_tiles + 3) / 4), (unsigned)groups), dim3(256), 0, stream,
+    hipLaunchKernelGGL(quant_h_kernel, dim3(xcd_quad_group_blocks((n_row_tiles + 3) / 4, groups)), dim3(256), 0, stream,
                        h, I, expert_off, E, capacity, expert_count, row2pair, amax2_part, n_part, n_row_tiles, codes,
                        scales, g, round_up ? 1 : 0);
     return hipGetLastError();

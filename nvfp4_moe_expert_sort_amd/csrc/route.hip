@@ -283,12 +283,16 @@ __global__ void __launch_bounds__(256) route_gather_kernel(int32_t H, int32_t K,
                                                            const float* __restrict__ gx, int64_t n_row_tiles,
                                                            uint8_t* __restrict__ a_codes,
                                                            uint8_t* __restrict__ a_scales, float* __restrict__ a_g) {
-    // Grid: x covers 32-row tiles (four per block, one per wave), y the
-    // pairs of 128-column steps.
+    // Block: four 32-row tiles (one per wave) x one group of kGatherSteps
+    // 128-column steps; the groups of a quad run together on one XCD
+    // (xcd_quad_group), so its rows' pairs and token rows are fetched once.
     const int lane = threadIdx.x & 63;
-    const int64_t rt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t cps = H / 128;
+    int64_t quad, grp;
+    if (!xcd_quad_group((n_row_tiles + 3) / 4, (cps + kGatherSteps - 1) / kGatherSteps, quad, grp)) return;
+    const int64_t rt = quad * 4 + (threadIdx.x >> 6);
     if (rt >= n_row_tiles) return;
-    const int64_t cps = H / 128, cp0 = (int64_t)blockIdx.y * kGatherSteps;
+    const int64_t cp0 = grp * kGatherSteps;
     const int q = lane & 7, step = q >> 2, ch = (q >> 1) & 1, hq = q & 1;  // this lane's 16-byte piece
     const int hs = lane >> 5, rs = lane & 31;                              // this lane's scale word
     int32_t pc[4];
@@ -352,7 +356,7 @@ hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* prob
     const int64_t rows_bound =
         capacity > 0 ? rows_cap : std::min<int64_t>(rows_cap, (P + (int64_t)E * (kMAlign - 1) + 31) / 32 * 32);
     const int64_t n_row_tiles = rows_bound / 32, groups = (H / 128 + kGatherSteps - 1) / kGatherSteps;
-    hipLaunchKernelGGL(route_gather_kernel, dim3((unsigned)((n_row_tiles + 3) / 4), (unsigned)groups), dim3(256), 0,
+    hipLaunchKernelGGL(route_gather_kernel, dim3(xcd_quad_group_blocks((n_row_tiles + 3) / 4, groups)), dim3(256), 0,
                        stream, H, K, rb.expert_off, E, capacity, rb.expert_count, rb.row2pair, rb.xq_codes, rb.xq_scales,
                        rb.gx, n_row_tiles, rb.a_codes, rb.a_scales, rb.a_g);
     return hipGetLastError();
