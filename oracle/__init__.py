@@ -93,6 +93,10 @@ def _load():
     lib.orc_moe_forward_w4a16.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P]
     lib.orc_moe_fc2.restype = None
     lib.orc_moe_fc2.argtypes = [P, I64, I64, I64, P, P, P, ctypes.c_int, ctypes.c_int, P]
+    lib.orc_silu_grad.restype = ctypes.c_double
+    lib.orc_silu_grad.argtypes = [ctypes.c_double]
+    lib.orc_moe_backward.restype = None
+    lib.orc_moe_backward.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.orc_route_masked.restype = I64
     lib.orc_route_masked.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P]
     lib.orc_moe_forward.restype = None
@@ -229,6 +233,46 @@ def route(ids: np.ndarray, n_experts: int, m_align: int):
     if P_pad < 0:
         raise ValueError("expert id out of range")
     return off, pair2row, row2pair[:P_pad].copy()
+
+
+def silu_grad(a: float) -> float:
+    """d silu / d a in FP64."""
+    return _load().orc_silu_grad(float(a))
+
+
+def moe_backward(x_bf16, ids, probs, w1_bf16, w2_bf16, y1, h, dout, intermediates: bool = False):
+    """The BF16 straight-through backward of the expert forward (miniTE page,
+    "how it differs": straight-through approximation, BF16 GEMMs on the stored
+    original BF16 activations and weights).  y1 [P, 2I] and h [P, I] are the
+    forward's BF16 FC1 output and FC2 input per pair; dout [T, H] BF16.
+    Returns (dx [T, H] BF16 bits, dprobs [T, K] f32, dW1 [E, 2I, H] f32,
+    dW2 [E, H, I] f32), plus dict(dh [P, I], dy1 [P, 2I]) with ``intermediates``."""
+    x = _c(x_bf16, np.uint16)
+    ids = _c(ids, np.int32)
+    probs = _c(probs, np.float32)
+    w1 = _c(w1_bf16, np.uint16)
+    w2 = _c(w2_bf16, np.uint16)
+    y1 = _c(y1, np.uint16)
+    h = _c(h, np.uint16)
+    dout = _c(dout, np.uint16)
+    T, H = x.shape
+    K = ids.shape[1]
+    E, twoI, _ = w1.shape
+    I = twoI // 2
+    assert w2.shape == (E, H, I) and y1.shape == (T * K, 2 * I) and h.shape == (T * K, I) and dout.shape == (T, H)
+    if ids.size and (ids.min() < 0 or ids.max() >= E):
+        raise ValueError("expert id out of range")
+    dx = np.empty((T, H), np.uint16)
+    dprobs = np.empty((T, K), np.float32)
+    dw1 = np.empty((E, 2 * I, H), np.float32)
+    dw2 = np.empty((E, H, I), np.float32)
+    dh = np.empty((T * K, I), np.uint16) if intermediates else None
+    dy1 = np.empty((T * K, 2 * I), np.uint16) if intermediates else None
+    _load().orc_moe_backward(_p(x), T, H, I, E, K, _p(ids), _p(probs), _p(w1), _p(w2), _p(y1), _p(h), _p(dout),
+                             _p(dx), _p(dprobs), _p(dw1), _p(dw2), _p(dh), _p(dy1))
+    if intermediates:
+        return dx, dprobs, dw1, dw2, dict(dh=dh, dy1=dy1)
+    return dx, dprobs, dw1, dw2
 
 
 def route_masked(ids: np.ndarray, n_experts: int, m_align: int, capacity: int):

@@ -601,3 +601,100 @@ void orc_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t
     free(w1d);
     free(w2d);
 }
+
+/* ------------------------------------------------------------------------ */
+/* BF16 straight-through backward                                            */
+/* ------------------------------------------------------------------------ */
+
+/* d silu / d a = sigmoid(a) (1 + a (1 - sigmoid(a))), in FP64. */
+double orc_silu_grad(double a) {
+    double sg = 1.0 / (1.0 + exp(-a));
+    return sg * (1.0 + a * (1.0 - sg));
+}
+
+/* The backward of the expert forward (miniTE page, "how it differs": the
+ * backward is the straight-through approximation -- quantization is taken as
+ * the identity -- computed by BF16 GEMMs on the stored original BF16
+ * activations and weights, so nothing is quantized in the backward).  With
+ * p = t*K + k, e = ids[p], gate/up the forward's BF16 FC1 outputs y1[p] and
+ * h[p] its BF16 FC2 input, per pair:
+ *   dh[p]     = bf16( dout[t] . W2[e] )                       FP64 sum over H
+ *   dgate[p]  = bf16( dh * prob * up * silu'(gate) )          FP64, elementwise
+ *   dup[p]    = bf16( dh * prob * silu(gate) )
+ *   dprob[p]  = fl32( sum_n dh[n] silu(gate[n]) up[n] )       FP64 sum over I
+ *   dxp[p]    = bf16( [dgate | dup] . W1[e] )                 FP64 sum over 2I
+ * and per token and expert:
+ *   dx[t]     = bf16( FP32 sum of dxp[t, k] over k = 0..K-1, from +0.0f )
+ *   dW2[e]    = fl32( sum over the pairs of e of dout[t]^T h[p] )      [H][I]
+ *   dW1[e]    = fl32( sum over the pairs of e of [dgate|dup]^T x[t] )  [2I][H]
+ * (the combine out[t] = sum_k y2[t, k] passes dout[t] to every slot; the
+ * router probability multiplies the SwiGLU output, so its gradient is the dot
+ * product of dh with silu(gate) up).  Weights w1 [E][2I][H], w2 [E][H][I] and
+ * x, y1, h, dout are BF16 bit patterns; dh_out [P][I] and dy1_out [P][2I]
+ * (BF16, may be NULL) return the intermediates. */
+void orc_moe_backward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, const int32_t* ids,
+                      const float* probs, const uint16_t* w1, const uint16_t* w2, const uint16_t* y1,
+                      const uint16_t* h, const uint16_t* dout, uint16_t* dx, float* dprobs, float* dw1, float* dw2,
+                      uint16_t* dh_out, uint16_t* dy1_out) {
+    int64_t P = T * K;
+    uint16_t* dh = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(P * I));
+    uint16_t* dy1 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(P * 2 * I));
+    uint16_t* dxp = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(P * H));
+    /* per pair: dh, the producer's gradients, dprob, the FC1 input gradient */
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t p = 0; p < P; p++) {
+        int64_t t = p / K, e = ids[p];
+        const uint16_t* w2e = w2 + e * H * I;
+        for (int64_t n = 0; n < I; n++) {
+            double acc = 0.0;
+            for (int64_t m = 0; m < H; m++)
+                acc += orc_bf16_to_double(dout[t * H + m]) * orc_bf16_to_double(w2e[m * I + n]);
+            dh[p * I + n] = orc_double_to_bf16(acc);
+        }
+        double pr = (double)probs[p], dp = 0.0;
+        for (int64_t n = 0; n < I; n++) {
+            double g = orc_bf16_to_double(y1[p * 2 * I + n]);
+            double u = orc_bf16_to_double(y1[p * 2 * I + I + n]);
+            double d = orc_bf16_to_double(dh[p * I + n]);
+            dy1[p * 2 * I + n] = orc_double_to_bf16(d * pr * u * orc_silu_grad(g));
+            dy1[p * 2 * I + I + n] = orc_double_to_bf16(d * pr * orc_silu(g));
+            dp += d * orc_silu(g) * u;
+        }
+        dprobs[p] = (float)dp;
+        const uint16_t* w1e = w1 + e * 2 * I * H;
+        for (int64_t m = 0; m < H; m++) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < 2 * I; j++)
+                acc += orc_bf16_to_double(dy1[p * 2 * I + j]) * orc_bf16_to_double(w1e[j * H + m]);
+            dxp[p * H + m] = orc_double_to_bf16(acc);
+        }
+    }
+    orc_combine(dxp, T, K, H, dx); /* FP32 slot-order sum, one BF16 rounding */
+    /* weight gradients: per expert, its pairs in increasing p */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t e = 0; e < E; e++) {
+        double* a1 = (double*)calloc((size_t)(2 * I * H), sizeof(double));
+        double* a2 = (double*)calloc((size_t)(H * I), sizeof(double));
+        for (int64_t p = 0; p < P; p++) {
+            if (ids[p] != e) continue;
+            int64_t t = p / K;
+            for (int64_t j = 0; j < 2 * I; j++) {
+                double d = orc_bf16_to_double(dy1[p * 2 * I + j]);
+                for (int64_t m = 0; m < H; m++) a1[j * H + m] += d * orc_bf16_to_double(x[t * H + m]);
+            }
+            for (int64_t m = 0; m < H; m++) {
+                double d = orc_bf16_to_double(dout[t * H + m]);
+                for (int64_t n = 0; n < I; n++) a2[m * I + n] += d * orc_bf16_to_double(h[p * I + n]);
+            }
+        }
+        for (int64_t i = 0; i < 2 * I * H; i++) dw1[e * 2 * I * H + i] = (float)a1[i];
+        for (int64_t i = 0; i < H * I; i++) dw2[e * H * I + i] = (float)a2[i];
+        free(a1);
+        free(a2);
+    }
+    if (dh_out) memcpy(dh_out, dh, sizeof(uint16_t) * (size_t)(P * I));
+    if (dy1_out) memcpy(dy1_out, dy1, sizeof(uint16_t) * (size_t)(P * 2 * I));
+    free(dh);
+    free(dy1);
+    free(dxp);
+}
