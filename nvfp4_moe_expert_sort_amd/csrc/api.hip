@@ -301,8 +301,11 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
                                 !w4a16);
     if (e != hipSuccess || !mark(1)) return NVFP4_E_HIP;
 
-    // Static bound on row tiles for this T (the device count is <= this).
-    const int64_t mt_bound = ((int64_t)T * K + E * (kMAlign - 1)) / kTileRows + E + 1;
+    // Static bounds for this T (the device counts are <= these): at most
+    // min(E, T*K) experts receive pairs, each padded by at most kMAlign - 1
+    // rows and ending in at most one partial row tile.
+    const int64_t P = (int64_t)T * K, used = std::min<int64_t>(E, P);
+    const int64_t mt_bound = (P + used * (kMAlign - 1)) / kTileRows + used + 1;
 
     if (w4a16) {
         // NVFP4 weights x BF16 activations: FC1 reads x's rows through
@@ -386,8 +389,12 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
         // Qwen3-30B-A3B-shaped layer at T = 4096: about 8 us faster than
         // persistent workgroups alone and 2-3 us faster than one workgroup
         // per tile; FC2's shorter tiles (K = I) are fastest persistent.
-        f1.persist = hybrid_persist();
-        e = launch_gemm(kGemmSwiGLU, f1, hybrid_grid(mt_bound * f1.n_tiles_n), s);
+        // Up to two rounds of tiles (decode-sized batches): one workgroup per
+        // tile, with no persistent part.
+        const int64_t fc1_tiles = mt_bound * f1.n_tiles_n;
+        const bool hybrid = fc1_tiles > 2 * (int64_t)hybrid_persist();
+        f1.persist = hybrid ? hybrid_persist() : 0;
+        e = launch_gemm(kGemmSwiGLU, f1, hybrid ? hybrid_grid(fc1_tiles) : (int)fc1_tiles, s);
         if (e != hipSuccess || !mark(2)) return NVFP4_E_HIP;
     }
 
@@ -396,7 +403,7 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     float* a2g = (float*)(ws + L.pub.a2_g);
     const int64_t rows_bound =
         capacity > 0 ? L.pub.rows_cap
-                     : std::min<int64_t>(L.pub.rows_cap, ((int64_t)T * K + E * (kMAlign - 1) + kMAlign - 1) / kMAlign * kMAlign);
+                     : std::min<int64_t>(L.pub.rows_cap, (P + used * (kMAlign - 1) + kMAlign - 1) / kMAlign * kMAlign);
     e = launch_quant_h(f1.out, rows_bound, I, rb.expert_off, (int32_t)E, capacity, rb.expert_count, rb.row2pair,
                        f1.amax_part, f1.n_part, a2c, a2s, a2g, ru, s);
     if (e != hipSuccess || !mark(3)) return NVFP4_E_HIP;

@@ -352,9 +352,12 @@ hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* prob
     st = hipGetLastError();
     if (st != hipSuccess) return st;
     if (!quant_x) return hipGetLastError();  // no quantized, sorted copy of X to build
-    // Row tiles that can hold rows for this T (the device offsets decide which are used).
+    // Row tiles that can hold rows for this T (the device offsets decide
+    // which are used): at most min(E, P) experts receive pairs, each padded
+    // by at most kMAlign - 1 rows.
+    const int64_t used = std::min<int64_t>(E, P);
     const int64_t rows_bound =
-        capacity > 0 ? rows_cap : std::min<int64_t>(rows_cap, (P + (int64_t)E * (kMAlign - 1) + 31) / 32 * 32);
+        capacity > 0 ? rows_cap : std::min<int64_t>(rows_cap, (P + used * (kMAlign - 1) + 31) / 32 * 32);
     const int64_t n_row_tiles = rows_bound / 32, groups = (H / 128 + kGatherSteps - 1) / kGatherSteps;
     hipLaunchKernelGGL(route_gather_kernel, dim3(xcd_quad_group_blocks((n_row_tiles + 3) / 4, groups)), dim3(256), 0,
                        stream, H, K, rb.expert_off, E, capacity, rb.expert_count, rb.row2pair, rb.xq_codes, rb.xq_scales,

@@ -194,6 +194,14 @@ def test_dense_linear(gpu, orc):
     out_r = to_host(m.linear(to_dev(wl.x[:M], dev), Wq, ws))
     torch.cuda.synchronize()
     assert np.array_equal(out_r, out[:M])
+    # three times the rows: enough row tiles for the 256-column tiles (4096 rows
+    # take the 128-column ones); the width changes no bit
+    xb = np.concatenate([wl.x] * 3)
+    wsb = torch.empty((m.linear_workspace_bytes(xb.shape[0], wl.K),), dtype=torch.uint8, device=dev)
+    out_b = to_host(m.linear(to_dev(xb, dev), Wq, wsb))
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert np.array_equal(out_b[i * wl.M:(i + 1) * wl.M], out)
 
 
 @pytest.fixture(scope="module")
