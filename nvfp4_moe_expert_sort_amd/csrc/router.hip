@@ -7,20 +7,23 @@
 // training side matches the rollout) and section 2 (the same discrete choice
 // needs the same tie-breaking and output order).
 //
-// One launch, one workgroup per 32 tokens:
-//   phase 1  logits[t][e] = sum_h x[t][h] w[e][h]: BF16 MFMA 32x32x16 with
-//            FP32 accumulation, one 32-expert tile per wave at a time, the
-//            full H in one fixed order, fragments loaded straight from
-//            memory (16 contiguous bytes per lane).  A token's scores come
-//            from the same instruction sequence whatever T is and wherever
-//            the token sits in its tile.
-//   phase 2  per token (one wavefront): 64-bit keys (order-preserving score
+// Two launches:
+//   scores   one wavefront per (32-token tile, 32-expert tile):
+//            logits[t][e] = sum_h x[t][h] w[e][h] by BF16 MFMA 32x32x16 with
+//            FP32 accumulation over the full H in one fixed order (increasing
+//            k), fragments loaded straight from memory (16 contiguous bytes
+//            per lane), the next 16 k-steps' loads in flight while the MFMAs
+//            of the current 16 run.  A token's scores come from the same
+//            instruction sequence whatever T is and wherever the token sits
+//            in its tile.
+//   top-k    one wavefront per token: 64-bit keys (order-preserving score
 //            bits, then the complement of the expert id, so equal scores go
 //            to the lower id); slot k gets the k-th expert of that total
 //            order.  Up to 256 experts each key's rank is counted against all
-//            keys at once; beyond that, K rounds of a wave-wide maximum.  Probabilities are the
-//            softmax restricted to the selection (renormalize) or over all
-//            experts, in FP32 with one fixed summation order.
+//            keys at once; beyond that, K rounds of a wave-wide maximum.
+//            Probabilities are the softmax restricted to the selection
+//            (renormalize) or over all experts, in FP32 with one fixed
+//            summation order.
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
 
@@ -54,155 +57,166 @@ __device__ __forceinline__ void count_ranks(const uint64_t* sk, int E2, const ui
     }
 }
 
-__global__ void __launch_bounds__(256) router_kernel(const uint16_t* __restrict__ x, int32_t T, int32_t H,
-                                                     const uint16_t* __restrict__ w, int32_t E, int32_t K,
-                                                     int renorm, float* __restrict__ logits,
-                                                     int32_t* __restrict__ ids, float* __restrict__ probs) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t t0 = (int64_t)blockIdx.x * kRouterTok;
+constexpr int kScoreSteps = 16;  // k-steps of 16 per load group; two groups in flight
 
-    // Phase 1.  MFMA operands: lane (kh*32 + r) supplies row r of the token
-    // tile (A) and of the expert tile (B), k = 8 kh .. 8 kh + 7 of the step.
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+router_scores_kernel(const uint16_t* __restrict__ x, int32_t T, int32_t H, const uint16_t* __restrict__ w,
+                     int32_t E, float* __restrict__ logits) {
+    const int lane = threadIdx.x & 63;
+    const int32_t n_et = (E + 31) / 32;
+    const int64_t t0 = (int64_t)(blockIdx.x / n_et) * kRouterTok;
+    const int32_t nt = blockIdx.x % n_et;
+    // MFMA operands: lane (kh*32 + r) supplies row r of the token tile (A)
+    // and of the expert tile (B), k = 8 kh .. 8 kh + 7 of the step.
     const int r = lane & 31, kh = lane >> 5;
     const int64_t tok = min(t0 + r, (int64_t)T - 1);  // rows past T read the last token, not stored
+    const int64_t e = min(nt * 32 + r, E - 1);         // columns past E read the last expert, not stored
     const uint16_t* xa = x + tok * H + 8 * kh;
-    for (int nt = wave; nt * 32 < E; nt += 4) {
-        const int64_t e = min(nt * 32 + r, E - 1);  // columns past E read the last expert, not stored
-        const uint16_t* wb = w + e * H + 8 * kh;
-        f32x16 acc = {};
-        // k-steps of 16 in groups of four, their loads issued together; the
-        // MFMAs run in increasing k either way
-        int k = 0;
-        for (; k + 64 <= H; k += 64) {
-            u32x4 a[4], b[4];
+    const uint16_t* wb = w + e * H + 8 * kh;
+    const int n = H / 16;
+    f32x16 acc = {};
+    // Group g's fragments are loaded while group g - 1's MFMAs run (steps past
+    // the end re-read the last one and run no MFMA); the MFMAs run in
+    // increasing k.
+    u32x4 a0[kScoreSteps], b0[kScoreSteps], a1[kScoreSteps], b1[kScoreSteps];
+    auto load = [&](int s0, u32x4 (&a)[kScoreSteps], u32x4 (&b)[kScoreSteps]) {
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                a[q] = *reinterpret_cast<const u32x4*>(xa + k + 16 * q);
-                b[q] = *reinterpret_cast<const u32x4*>(wb + k + 16 * q);
-            }
+        for (int q = 0; q < kScoreSteps; q++) {
+            const int k = 16 * min(s0 + q, n - 1);
+            a[q] = *reinterpret_cast<const u32x4*>(xa + k);
+            b[q] = *reinterpret_cast<const u32x4*>(wb + k);
+        }
+    };
+    auto mfma = [&](int s0, const u32x4 (&a)[kScoreSteps], const u32x4 (&b)[kScoreSteps]) {
 #pragma unroll
-            for (int q = 0; q < 4; q++)
+        for (int q = 0; q < kScoreSteps; q++)
+            if (s0 + q < n)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[q]),
                                                               __builtin_bit_cast(bf16x8, b[q]), acc, 0, 0, 0);
-        }
-        for (; k < H; k += 16) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xa + k));
-            const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wb + k));
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-        }
-        // register j: row (j/4)*8 + kh*4 + j%4 of the token tile, column r
-        const int col = nt * 32 + r;
+    };
+    load(0, a0, b0);
+    for (int s0 = 0; s0 < n; s0 += 2 * kScoreSteps) {
+        load(s0 + kScoreSteps, a1, b1);
+        mfma(s0, a0, b0);
+        load(s0 + 2 * kScoreSteps, a0, b0);
+        mfma(s0 + kScoreSteps, a1, b1);
+    }
+    // register j: row (j/4)*8 + kh*4 + j%4 of the token tile, column r
+    const int col = nt * 32 + r;
 #pragma unroll
-        for (int j = 0; j < 16; j++) {
-            const int64_t t = t0 + (j >> 2) * 8 + kh * 4 + (j & 3);
-            if (t < T && col < E) logits[t * E + col] = acc[j];
+    for (int j = 0; j < 16; j++) {
+        const int64_t t = t0 + (j >> 2) * 8 + kh * 4 + (j & 3);
+        if (t < T && col < E) logits[t * E + col] = acc[j];
+    }
+}
+
+constexpr int kTopkWaves = 4;  // tokens per workgroup of the top-k kernel (one wavefront each)
+
+__global__ void __launch_bounds__(kTopkWaves * 64) router_topk_kernel(int32_t T, int32_t E, int32_t K, int renorm,
+                                                                     const float* __restrict__ logits,
+                                                                     int32_t* __restrict__ ids,
+                                                                     float* __restrict__ probs) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * kTopkWaves + wave;
+    __shared__ __attribute__((aligned(16))) uint64_t skey[kTopkWaves][kRankMaxE];
+    __shared__ uint64_t ssel[kTopkWaves][kMaxTopK];
+    if (t >= T) return;
+    const bool by_rank = E <= kRankMaxE;
+    const float* lt = logits + t * E;
+    uint64_t key[kRouterKeys];
+#pragma unroll
+    for (int i = 0; i < kRouterKeys; i++) {
+        const int e = i * kWave + lane;
+        key[i] = e < E ? ((uint64_t)score_order(lt[e]) << 32) | (uint32_t)~(uint32_t)e : 0ull;
+    }
+    int my_e = 0;
+    float my_l = 0.0f;
+    if (by_rank) {
+        // The keys are unique, so a key's place in the order is the number of
+        // larger keys; slot k takes the key of rank k.  Every lane counts
+        // against all E keys (read back through LDS as broadcasts), so no
+        // round waits on another.  Only the lane's live keys are ranked
+        // (ceil(E / 64) of them), two keys per LDS read (an odd E is padded
+        // with a zero key, which never outranks a real one).
+        constexpr int kR = kRankMaxE / kWave;
+        const int E2 = (E + 1) & ~1;
+#pragma unroll
+        for (int i = 0; i < kR; i++) {
+            const int e = i * kWave + lane;
+            if (e < E2) skey[wave][e] = e < E ? key[i] : 0ull;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        int rank[kR];
+#pragma unroll
+        for (int i = 0; i < kR; i++) rank[i] = 0;
+        const int nk = (E + kWave - 1) / kWave;
+        if (nk == 1)
+            count_ranks<1>(&skey[wave][0], E2, key, rank);
+        else if (nk == 2)
+            count_ranks<2>(&skey[wave][0], E2, key, rank);
+        else
+            count_ranks<4>(&skey[wave][0], E2, key, rank);
+#pragma unroll
+        for (int i = 0; i < kR; i++) {
+            const int e = i * kWave + lane;
+            if (e < E && rank[i] < K) ssel[wave][rank[i]] = key[i];
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+        if (lane < K) {
+            const uint64_t b = ssel[wave][lane];
+            my_e = (int)~(uint32_t)b;
+            my_l = score_value((uint32_t)(b >> 32));
         }
     }
-    __syncthreads();  // this workgroup's scores are written (workgroup-scope fence included)
-
-    // Phase 2: wave w takes tokens w, w + 4, ... of the tile.
-    __shared__ __attribute__((aligned(16))) uint64_t skey[4][kRankMaxE];
-    __shared__ uint64_t ssel[4][kMaxTopK];
-    const bool by_rank = E <= kRankMaxE;
-    for (int tl = wave; tl < kRouterTok; tl += 4) {
-        const int64_t t = t0 + tl;
-        if (t >= T) break;
-        const float* lt = logits + t * E;
-        uint64_t key[kRouterKeys];
+    for (int k = 0; !by_rank && k < K; k++) {
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int i = 0; i < kRouterKeys; i++) best = key[i] > best ? key[i] : best;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const uint64_t u = __shfl_xor(best, o, kWave);
+            best = u > best ? u : best;
+        }
+#pragma unroll
+        for (int i = 0; i < kRouterKeys; i++)
+            if (key[i] == best) key[i] = 0ull;  // keys are unique: one owner
+        if (lane == k) {
+            my_e = (int)~(uint32_t)best;
+            my_l = score_value((uint32_t)(best >> 32));
+        }
+    }
+    const float top = __shfl(my_l, 0, kWave);
+    const float num = lane < K ? expf(my_l - top) : 0.0f;
+    float den = 0.0f;
+    if (renorm) {
+        for (int k = 0; k < K; k++) den += __shfl(num, k, kWave);  // slot order
+    } else {
+        // this lane's experts in increasing order, then a fixed butterfly
 #pragma unroll
         for (int i = 0; i < kRouterKeys; i++) {
             const int e = i * kWave + lane;
-            key[i] = e < E ? ((uint64_t)score_order(lt[e]) << 32) | (uint32_t)~(uint32_t)e : 0ull;
+            if (e < E) den += expf(lt[e] - top);
         }
-        int my_e = 0;
-        float my_l = 0.0f;
-        if (by_rank) {
-            // The keys are unique, so a key's place in the order is the number
-            // of larger keys; slot k takes the key of rank k.  Every lane
-            // counts against all E keys (read back through LDS as broadcasts),
-            // so no round waits on another.
-            // Only the lane's live keys are ranked (ceil(E / 64) of them), two
-            // keys per LDS read (an odd E is padded with a zero key, which
-            // never outranks a real one).
-            constexpr int kR = kRankMaxE / kWave;
-            const int E2 = (E + 1) & ~1;
 #pragma unroll
-            for (int i = 0; i < kR; i++) {
-                const int e = i * kWave + lane;
-                if (e < E2) skey[wave][e] = e < E ? key[i] : 0ull;
-            }
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
-            __builtin_amdgcn_wave_barrier();
-            int rank[kR];
-#pragma unroll
-            for (int i = 0; i < kR; i++) rank[i] = 0;
-            const int nk = (E + kWave - 1) / kWave;
-            if (nk == 1)
-                count_ranks<1>(&skey[wave][0], E2, key, rank);
-            else if (nk == 2)
-                count_ranks<2>(&skey[wave][0], E2, key, rank);
-            else
-                count_ranks<4>(&skey[wave][0], E2, key, rank);
-#pragma unroll
-            for (int i = 0; i < kR; i++) {
-                const int e = i * kWave + lane;
-                if (e < E && rank[i] < K) ssel[wave][rank[i]] = key[i];
-            }
-            __builtin_amdgcn_s_waitcnt(0xC07F);
-            __builtin_amdgcn_wave_barrier();
-            if (lane < K) {
-                const uint64_t b = ssel[wave][lane];
-                my_e = (int)~(uint32_t)b;
-                my_l = score_value((uint32_t)(b >> 32));
-            }
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // read before the next token's keys overwrite them
-            __builtin_amdgcn_wave_barrier();
-        }
-        for (int k = 0; !by_rank && k < K; k++) {
-            uint64_t best = 0ull;
-#pragma unroll
-            for (int i = 0; i < kRouterKeys; i++) best = key[i] > best ? key[i] : best;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                const uint64_t u = __shfl_xor(best, o, kWave);
-                best = u > best ? u : best;
-            }
-#pragma unroll
-            for (int i = 0; i < kRouterKeys; i++)
-                if (key[i] == best) key[i] = 0ull;  // keys are unique: one owner
-            if (lane == k) {
-                my_e = (int)~(uint32_t)best;
-                my_l = score_value((uint32_t)(best >> 32));
-            }
-        }
-        const float top = __shfl(my_l, 0, kWave);
-        const float num = lane < K ? expf(my_l - top) : 0.0f;
-        float den = 0.0f;
-        if (renorm) {
-            for (int k = 0; k < K; k++) den += __shfl(num, k, kWave);  // slot order
-        } else {
-            // this lane's experts in increasing order, then a fixed butterfly
-#pragma unroll
-            for (int i = 0; i < kRouterKeys; i++) {
-                const int e = i * kWave + lane;
-                if (e < E) den += expf(lt[e] - top);
-            }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, kWave);
-        }
-        if (lane < K) {
-            ids[t * K + lane] = my_e;
-            probs[t * K + lane] = num / den;
-        }
+        for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, kWave);
+    }
+    if (lane < K) {
+        ids[t * K + lane] = my_e;
+        probs[t * K + lane] = num / den;
     }
 }
 
 hipError_t launch_router(const uint16_t* x, int32_t T, int32_t H, const uint16_t* w, int32_t E, int32_t K,
                          bool renorm, float* logits, int32_t* ids, float* probs, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    const unsigned blocks = (unsigned)((T + kRouterTok - 1) / kRouterTok);
-    hipLaunchKernelGGL(router_kernel, dim3(blocks), dim3(256), 0, stream, x, T, H, w, E, K, renorm ? 1 : 0, logits,
-                       ids, probs);
+    const unsigned score_waves = (unsigned)(((T + kRouterTok - 1) / kRouterTok) * ((E + 31) / 32));
+    hipLaunchKernelGGL(router_scores_kernel, dim3(score_waves), dim3(64), 0, stream, x, T, H, w, E, logits);
+    hipError_t st = hipGetLastError();
+    if (st != hipSuccess) return st;
+    hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)((T + kTopkWaves - 1) / kTopkWaves)), dim3(kTopkWaves * 64),
+                       0, stream, T, E, K, renorm ? 1 : 0, logits, ids, probs);
     return hipGetLastError();
 }
 
