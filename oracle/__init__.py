@@ -97,6 +97,10 @@ def _load():
     lib.orc_silu_grad.argtypes = [ctypes.c_double]
     lib.orc_moe_backward.restype = None
     lib.orc_moe_backward.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.orc_swiglu_backward.restype = None
+    lib.orc_swiglu_backward.argtypes = [P, P, P, I64, I64, P, P]
+    lib.orc_moe_weight_grads.restype = None
+    lib.orc_moe_weight_grads.argtypes = [P, P, I64, I64, I64, I64, I64, P, P, P, P, P]
     lib.orc_route_masked.restype = I64
     lib.orc_route_masked.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P]
     lib.orc_moe_forward.restype = None
@@ -273,6 +277,38 @@ def moe_backward(x_bf16, ids, probs, w1_bf16, w2_bf16, y1, h, dout, intermediate
     if intermediates:
         return dx, dprobs, dw1, dw2, dict(dh=dh, dy1=dy1)
     return dx, dprobs, dw1, dw2
+
+
+def swiglu_backward(dh, y1, p):
+    """SwiGLU backward per row (the backward's producer step): (dy1 [R, 2I] BF16 bits, dprob [R] f32)."""
+    dh = _c(dh, np.uint16)
+    y1 = _c(y1, np.uint16)
+    p = _c(p, np.float32).reshape(-1)
+    R, I = dh.shape
+    assert y1.shape == (R, 2 * I) and p.size == R
+    dy1 = np.empty((R, 2 * I), np.uint16)
+    dprob = np.empty((R,), np.float32)
+    _load().orc_swiglu_backward(_p(dh), _p(y1), _p(p), R, I, _p(dy1), _p(dprob))
+    return dy1, dprob
+
+
+def moe_weight_grads(x_bf16, dout, ids, dy1, h, n_experts: int):
+    """Weight gradients from given per-pair gradients (the backward's last step):
+    (dW1 [E, 2I, H] f32, dW2 [E, H, I] f32), sums over each expert's pairs in
+    increasing pair order in FP64."""
+    x = _c(x_bf16, np.uint16)
+    dout = _c(dout, np.uint16)
+    ids = _c(ids, np.int32)
+    dy1 = _c(dy1, np.uint16)
+    h = _c(h, np.uint16)
+    T, H = x.shape
+    K = ids.shape[1]
+    I = h.shape[1]
+    E = int(n_experts)
+    dw1 = np.empty((E, 2 * I, H), np.float32)
+    dw2 = np.empty((E, H, I), np.float32)
+    _load().orc_moe_weight_grads(_p(x), _p(dout), T, H, I, E, K, _p(ids), _p(dy1), _p(h), _p(dw1), _p(dw2))
+    return dw1, dw2
 
 
 def route_masked(ids: np.ndarray, n_experts: int, m_align: int, capacity: int):

@@ -612,6 +612,60 @@ double orc_silu_grad(double a) {
     return sg * (1.0 + a * (1.0 - sg));
 }
 
+/* SwiGLU backward of R rows (miniTE page, "how it differs": router
+ * probability on the SwiGLU output): from dh [R][I] (BF16), the forward's
+ * y1 [R][2I] = [gate | up] (BF16) and p [R]:
+ *   dgate = bf16(dh p up silu'(gate)),  dup = bf16(dh p silu(gate))   in dy1 [R][2I]
+ *   dprob = fl32(sum_n dh silu(gate) up)                               in dprob [R]
+ * all in FP64. */
+void orc_swiglu_backward(const uint16_t* dh, const uint16_t* y1, const float* p, int64_t R, int64_t I, uint16_t* dy1,
+                         float* dprob) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; r++) {
+        double pr = (double)p[r], dp = 0.0;
+        for (int64_t n = 0; n < I; n++) {
+            double g = orc_bf16_to_double(y1[r * 2 * I + n]);
+            double u = orc_bf16_to_double(y1[r * 2 * I + I + n]);
+            double d = orc_bf16_to_double(dh[r * I + n]);
+            dy1[r * 2 * I + n] = orc_double_to_bf16(d * pr * u * orc_silu_grad(g));
+            dy1[r * 2 * I + I + n] = orc_double_to_bf16(d * pr * orc_silu(g));
+            dp += d * orc_silu(g) * u;
+        }
+        dprob[r] = (float)dp;
+    }
+}
+
+/* Weight gradients from given per-pair gradients: for each expert e, over its
+ * pairs p = t*K + k in increasing p, in FP64, stored as FP32:
+ *   dw1[e] = sum dy1[p]^T x[t]   [2I][H],    dw2[e] = sum dy2[t]^T h[p]   [H][I]
+ * with dy2[t] = dout[t] (the combine's gradient).  All inputs BF16. */
+void orc_moe_weight_grads(const uint16_t* x, const uint16_t* dout, int64_t T, int64_t H, int64_t I, int64_t E,
+                          int64_t K, const int32_t* ids, const uint16_t* dy1, const uint16_t* h, float* dw1,
+                          float* dw2) {
+    int64_t P = T * K;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t e = 0; e < E; e++) {
+        double* a1 = (double*)calloc((size_t)(2 * I * H), sizeof(double));
+        double* a2 = (double*)calloc((size_t)(H * I), sizeof(double));
+        for (int64_t p = 0; p < P; p++) {
+            if (ids[p] != e) continue;
+            int64_t t = p / K;
+            for (int64_t j = 0; j < 2 * I; j++) {
+                double d = orc_bf16_to_double(dy1[p * 2 * I + j]);
+                for (int64_t m = 0; m < H; m++) a1[j * H + m] += d * orc_bf16_to_double(x[t * H + m]);
+            }
+            for (int64_t m = 0; m < H; m++) {
+                double d = orc_bf16_to_double(dout[t * H + m]);
+                for (int64_t n = 0; n < I; n++) a2[m * I + n] += d * orc_bf16_to_double(h[p * I + n]);
+            }
+        }
+        for (int64_t i = 0; i < 2 * I * H; i++) dw1[e * 2 * I * H + i] = (float)a1[i];
+        for (int64_t i = 0; i < H * I; i++) dw2[e * H * I + i] = (float)a2[i];
+        free(a1);
+        free(a2);
+    }
+}
+
 /* The backward of the expert forward (miniTE page, "how it differs": the
  * backward is the straight-through approximation -- quantization is taken as
  * the identity -- computed by BF16 GEMMs on the stored original BF16
@@ -640,7 +694,7 @@ void orc_moe_backward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_
     uint16_t* dh = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(P * I));
     uint16_t* dy1 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(P * 2 * I));
     uint16_t* dxp = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(P * H));
-    /* per pair: dh, the producer's gradients, dprob, the FC1 input gradient */
+    /* per pair: dh */
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t p = 0; p < P; p++) {
         int64_t t = p / K, e = ids[p];
@@ -651,17 +705,13 @@ void orc_moe_backward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_
                 acc += orc_bf16_to_double(dout[t * H + m]) * orc_bf16_to_double(w2e[m * I + n]);
             dh[p * I + n] = orc_double_to_bf16(acc);
         }
-        double pr = (double)probs[p], dp = 0.0;
-        for (int64_t n = 0; n < I; n++) {
-            double g = orc_bf16_to_double(y1[p * 2 * I + n]);
-            double u = orc_bf16_to_double(y1[p * 2 * I + I + n]);
-            double d = orc_bf16_to_double(dh[p * I + n]);
-            dy1[p * 2 * I + n] = orc_double_to_bf16(d * pr * u * orc_silu_grad(g));
-            dy1[p * 2 * I + I + n] = orc_double_to_bf16(d * pr * orc_silu(g));
-            dp += d * orc_silu(g) * u;
-        }
-        dprobs[p] = (float)dp;
-        const uint16_t* w1e = w1 + e * 2 * I * H;
+    }
+    /* the SwiGLU backward and the router-probability gradient */
+    orc_swiglu_backward(dh, y1, probs, P, I, dy1, dprobs);
+    /* per pair: the FC1 input gradient; per token: the slot-order sum */
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t p = 0; p < P; p++) {
+        const uint16_t* w1e = w1 + (int64_t)ids[p] * 2 * I * H;
         for (int64_t m = 0; m < H; m++) {
             double acc = 0.0;
             for (int64_t j = 0; j < 2 * I; j++)
@@ -671,27 +721,7 @@ void orc_moe_backward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_
     }
     orc_combine(dxp, T, K, H, dx); /* FP32 slot-order sum, one BF16 rounding */
     /* weight gradients: per expert, its pairs in increasing p */
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t e = 0; e < E; e++) {
-        double* a1 = (double*)calloc((size_t)(2 * I * H), sizeof(double));
-        double* a2 = (double*)calloc((size_t)(H * I), sizeof(double));
-        for (int64_t p = 0; p < P; p++) {
-            if (ids[p] != e) continue;
-            int64_t t = p / K;
-            for (int64_t j = 0; j < 2 * I; j++) {
-                double d = orc_bf16_to_double(dy1[p * 2 * I + j]);
-                for (int64_t m = 0; m < H; m++) a1[j * H + m] += d * orc_bf16_to_double(x[t * H + m]);
-            }
-            for (int64_t m = 0; m < H; m++) {
-                double d = orc_bf16_to_double(dout[t * H + m]);
-                for (int64_t n = 0; n < I; n++) a2[m * I + n] += d * orc_bf16_to_double(h[p * I + n]);
-            }
-        }
-        for (int64_t i = 0; i < 2 * I * H; i++) dw1[e * 2 * I * H + i] = (float)a1[i];
-        for (int64_t i = 0; i < H * I; i++) dw2[e * H * I + i] = (float)a2[i];
-        free(a1);
-        free(a2);
-    }
+    orc_moe_weight_grads(x, dout, T, H, I, E, K, ids, dy1, h, dw1, dw2);
     if (dh_out) memcpy(dh_out, dh, sizeof(uint16_t) * (size_t)(P * I));
     if (dy1_out) memcpy(dy1_out, dy1, sizeof(uint16_t) * (size_t)(P * 2 * I));
     free(dh);

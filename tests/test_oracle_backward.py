@@ -157,3 +157,24 @@ def test_special_cases(orc):
     g, u = _v(y1[2, :16]), _v(y1[2, 16:])
     want = float(np.sum(_v(mid["dh"][2]) * (g / (1 + np.exp(-g))) * u))
     assert abs(float(dp0[1, 0]) - want) <= 1e-6 * abs(want)
+
+
+def test_backward_is_the_composition_of_its_steps(orc):
+    """moe_backward equals its steps run one at a time: dh (exact-pinned GEMM),
+    swiglu_backward, each pair's FC1 input gradient, the combine, and
+    moe_weight_grads."""
+    x, w1, w2, ids, probs, y1, h, dout = _case(5, T=5, H=32, I=16, E=3, K=2)
+    dx, dprobs, dw1, dw2, mid = orc.moe_backward(x, ids, probs, w1, w2, y1, h, dout, intermediates=True)
+    dy1, dprob = orc.swiglu_backward(mid["dh"], y1, probs)
+    assert np.array_equal(dy1, mid["dy1"]) and np.array_equal(dprob.view(np.uint32), dprobs.reshape(-1).view(np.uint32))
+    g1, g2 = orc.moe_weight_grads(x, dout, ids, mid["dy1"], h, w1.shape[0])
+    assert np.array_equal(g1, dw1) and np.array_equal(g2, dw2)
+    # FC1 input gradient per pair, then the slot-order combine
+    T, K = ids.shape
+    dxp = np.zeros((T, K, x.shape[1]), np.uint16)
+    for t in range(T):
+        for k in range(K):
+            e = int(ids[t, k])
+            dxp[t, k] = orc.gemm_epilogue(_v(mid["dy1"][t * K + k:t * K + k + 1]), np.ones(1, np.float32),
+                                          _v(w1[e]).T.copy(), np.ones(x.shape[1], np.float32))[0]
+    assert np.array_equal(orc.combine(dxp), dx)
