@@ -193,6 +193,38 @@ NVFP4MOE_API int nvfp4moe_moe_expert_forward_unfused(const nvfp4moe_config* cfg,
                                                      int64_t y1_rows, void* workspace, size_t workspace_bytes,
                                                      void* stream);
 
+/* The BF16 straight-through backward of the expert forward (miniTE page,
+ * "how it differs": the backward takes quantization as the identity and runs
+ * BF16 GEMMs on the stored original BF16 activations and weights, avoiding
+ * any quantization on the way back).  It follows a call of
+ * nvfp4moe_moe_expert_forward_unfused on the same cfg, x and T, whose
+ * workspace (sort metadata, row probabilities, h) and y1 it reads.  With
+ * p = t*K + k, e = ids[t,k], gate/up = y1 of pair p and h its FC2 input:
+ *   dh[p]     = bf16(dout[t] . W2[e])             FP32 accumulation
+ *   dgate[p]  = bf16(dh prob up silu'(gate)),  dup[p] = bf16(dh prob silu(gate))
+ *   dprobs[t,k] = sum_n dh silu(gate) up         FP32
+ *   dx[t]     = bf16(FP32 sum over k = 0..K-1, in slot order, of
+ *               bf16([dgate | dup] . W1[e]))
+ *   dw1[e]    = sum over e's pairs of [dgate | dup]^T x[t]      FP32 [2I, H]
+ *   dw2[e]    = sum over e's pairs of dout[t]^T h[p]            FP32 [H, I]
+ * (the combine passes dout[t] to every slot).  Every sum is one fixed order
+ * (deterministic); dx[t] depends only on token t's inputs.
+ *   x, dout   [T, H] BF16; w1 [E, 2I, H] and w2 [E, H, I] the BF16 weights
+ *             the quantized ones were made from (16-byte aligned)
+ *   y1        the forward's y1 buffer, y1_rows >= rows_cap
+ *   fwd_workspace   the forward's workspace (read only)
+ *   dx [T, H] BF16, dprobs [T, K] FP32, dw1, dw2 FP32: caller-owned outputs
+ *             (dw1, dw2 overwritten, experts without tokens get zeros)
+ *   workspace nvfp4moe_backward_workspace_bytes(cfg) bytes (dh, dgate|dup
+ *             and each pair's FC1 input gradient), 256-byte aligned
+ * Contiguous row layout only; errors as for the forward; no synchronisation. */
+NVFP4MOE_API size_t nvfp4moe_backward_workspace_bytes(const nvfp4moe_config* cfg);
+NVFP4MOE_API int nvfp4moe_moe_expert_backward(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T,
+                                              const uint16_t* w1, const uint16_t* w2, const uint16_t* y1,
+                                              int64_t y1_rows, const void* fwd_workspace, size_t fwd_workspace_bytes,
+                                              const uint16_t* dout, uint16_t* dx, float* dprobs, float* dw1,
+                                              float* dw2, void* workspace, size_t workspace_bytes, void* stream);
+
 /* The W4A16 variant of the expert forward (the article, section 6: NVFP4
  * W4A16 routed experts): the same sort, SwiGLU producer, combine, arguments,
  * workspace and errors as nvfp4moe_moe_expert_forward, with the activations

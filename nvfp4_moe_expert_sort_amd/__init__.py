@@ -29,7 +29,7 @@ EXPORTS = ["nvfp4_status_str", "nvfp4_quantize", "nvfp4moe_weight_bytes", "nvfp4
            "nvfp4moe_device_error",
            "nvfp4moe_workspace_layout", "nvfp4moe_workspace_bytes_masked", "nvfp4moe_workspace_layout_masked",
            "nvfp4moe_moe_expert_forward_masked", "nvfp4moe_moe_expert_forward_unfused",
-           "nvfp4moe_moe_expert_forward_noalloc",
+           "nvfp4moe_moe_expert_forward_noalloc", "nvfp4moe_backward_workspace_bytes", "nvfp4moe_moe_expert_backward",
            "nvfp4moe_moe_expert_forward_w4a16", "nvfp4moe_router_topk", "nvfp4_linear_workspace_bytes", "nvfp4_linear",
            "nvfp4moe_selftest_batch_invariance"]
 
@@ -86,6 +86,9 @@ def lib():
         "nvfp4moe_workspace_layout_masked": (ctypes.c_int, [cfgp, i32, ctypes.POINTER(WsLayout)]),
         "nvfp4moe_moe_expert_forward_masked": (ctypes.c_int, [cfgp, i32, vp, i32, vp, vp, qtp, qtp, vp, vp, sz, vp]),
         "nvfp4moe_moe_expert_forward_w4a16": (ctypes.c_int, [cfgp, vp, i32, vp, vp, qtp, qtp, vp, vp, sz, vp]),
+        "nvfp4moe_backward_workspace_bytes": (sz, [cfgp]),
+        "nvfp4moe_moe_expert_backward": (ctypes.c_int, [cfgp, vp, i32, vp, vp, vp, i64, vp, sz, vp, vp, vp, vp, vp, vp,
+                                                         sz, vp]),
         "nvfp4moe_moe_expert_forward_noalloc": (ctypes.c_int, [cfgp, vp, i32, vp, vp, qtp, qtp, vp, vp, vp]),
         "nvfp4moe_moe_expert_forward_unfused": (ctypes.c_int, [cfgp, vp, i32, vp, vp, qtp, qtp, vp, vp, i64, vp, sz,
                                                                 vp]),
@@ -234,6 +237,29 @@ def moe_expert_forward_w4a16(cfg: Config, x, ids, probs, weights: QuantWeights, 
                                                  _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "nvfp4moe_moe_expert_forward_w4a16")
     return out
+
+
+def moe_expert_backward(cfg: Config, x, w1, w2, y1, fwd_workspace, dout, stream=None):
+    """nvfp4moe_moe_expert_backward after moe_expert_forward_unfused(cfg, x, ...) filled fwd_workspace and
+    y1: BF16 w1 [E, 2I, H], w2 [E, H, I], dout [T, H] -> (dx [T, H] BF16, dprobs [T, K] f32,
+    dw1 [E, 2I, H] f32, dw2 [E, H, I] f32)."""
+    import torch
+    T = x.shape[0]
+    E, H, I, K = cfg.n_experts, cfg.hidden, cfg.inter, cfg.top_k
+    dev = x.device
+    dx = torch.empty((T, H), dtype=x.dtype, device=dev)
+    dprobs = torch.empty((T, K), dtype=torch.float32, device=dev)
+    dw1 = torch.empty((E, 2 * I, H), dtype=torch.float32, device=dev)
+    dw2 = torch.empty((E, H, I), dtype=torch.float32, device=dev)
+    n = lib().nvfp4moe_backward_workspace_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise Nvfp4Error(2, "nvfp4moe_backward_workspace_bytes")
+    ws = torch.empty((n,), dtype=torch.uint8, device=dev)
+    st = lib().nvfp4moe_moe_expert_backward(ctypes.byref(cfg), _ptr(x), T, _ptr(w1), _ptr(w2), _ptr(y1), y1.shape[0],
+                                            _ptr(fwd_workspace), fwd_workspace.numel(), _ptr(dout), _ptr(dx),
+                                            _ptr(dprobs), _ptr(dw1), _ptr(dw2), _ptr(ws), n, _stream(stream))
+    _check(st, "nvfp4moe_moe_expert_backward")
+    return dx, dprobs, dw1, dw2, ws
 
 
 def moe_expert_forward_noalloc(cfg: Config, x, ids, probs, weights: QuantWeights, out=None, err_word=None,

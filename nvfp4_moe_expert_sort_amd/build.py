@@ -9,8 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "lib", "libnvfp4moe.so")
-SOURCES = ["quant.hip", "route.hip", "gemm.hip", "gemm_w4a16.hip", "producer.hip", "combine.hip", "router.hip",
-           "api.hip", "selftest.hip"]
+SOURCES = ["quant.hip", "route.hip", "gemm.hip", "gemm_w4a16.hip", "producer.hip", "backward.hip", "combine.hip",
+           "router.hip", "api.hip", "selftest.hip"]
 
 # -ffp-contract=off and no fast-math: the quantizer's binary32 divisions and
 # products must be the IEEE operations the numeric contract names.  Packed

@@ -494,6 +494,68 @@ int nvfp4moe_moe_expert_forward_unfused(const nvfp4moe_config* cfg, const uint16
                         T > 0 ? y1 : nullptr);
 }
 
+size_t nvfp4moe_backward_workspace_bytes(const nvfp4moe_config* cfg) {
+    if (!cfg_ok(cfg)) return 0;
+    const size_t rows = (size_t)make_layout(cfg).pub.rows_cap;
+    const size_t I = cfg->inter, H = cfg->hidden;
+    return up(rows * I * 2, kAlign) + up(rows * 2 * I * 2, kAlign) + up(rows * H * 2, kAlign);
+}
+
+int nvfp4moe_moe_expert_backward(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const uint16_t* w1,
+                                 const uint16_t* w2, const uint16_t* y1, int64_t y1_rows, const void* fwd_workspace,
+                                 size_t fwd_workspace_bytes, const uint16_t* dout, uint16_t* dx, float* dprobs,
+                                 float* dw1, float* dw2, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!cfg) return NVFP4_E_NULL;
+    if (!cfg_ok(cfg)) return NVFP4_E_SHAPE;
+    if (T < 0) return NVFP4_E_SHAPE;
+    if (T > cfg->max_tokens) return NVFP4_E_CAPACITY;
+    const Layout L = make_layout(cfg);
+    if (y1_rows < L.pub.rows_cap) return NVFP4_E_SHAPE;
+    if (!fwd_workspace || !workspace) return NVFP4_E_NULL;
+    if (fwd_workspace_bytes < L.total || workspace_bytes < nvfp4moe_backward_workspace_bytes(cfg))
+        return NVFP4_E_WORKSPACE;
+    if (!aligned(fwd_workspace, kAlign) || !aligned(workspace, kAlign)) return NVFP4_E_ALIGN;
+    if (T == 0) return NVFP4_OK;
+    if (!x || !w1 || !w2 || !y1 || !dout || !dx || !dprobs || !dw1 || !dw2) return NVFP4_E_NULL;
+    if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(y1, 16) || !aligned(dout, 16) ||
+        !aligned(dx, 16) || !aligned(dprobs, 4) || !aligned(dw1, 4) || !aligned(dw2, 4))
+        return NVFP4_E_ALIGN;
+    const int64_t E = cfg->n_experts, K = cfg->top_k, H = cfg->hidden, I = cfg->inter;
+    const uint8_t* fw = (const uint8_t*)fwd_workspace;
+    uint8_t* ws = (uint8_t*)workspace;
+    const size_t rows = (size_t)L.pub.rows_cap;
+    BwdArgs A{};
+    A.T = T;
+    A.top_k = (int32_t)K;
+    A.E = E;
+    A.H = H;
+    A.I = I;
+    A.x = x;
+    A.w1 = w1;
+    A.w2 = w2;
+    A.y1 = y1;
+    A.h = (const uint16_t*)(fw + L.pub.h);
+    A.dout = dout;
+    A.row2pair = (const int32_t*)(fw + L.pub.row2pair);
+    A.pair2row = (const int32_t*)(fw + L.pub.pair2row);
+    A.row_prob = (const float*)(fw + L.row_prob);
+    A.mtiles = (const int4*)(fw + L.mtiles);
+    A.n_mtiles = (const int32_t*)(fw + L.n_mtiles);
+    A.expert_off = (const int32_t*)(fw + L.pub.expert_off);
+    A.expert_count = (const int32_t*)(fw + L.pub.expert_count);
+    const int64_t P = (int64_t)T * K, used = std::min<int64_t>(E, P);
+    A.mt_bound = (P + used * (kMAlign - 1)) / kTileRows + used + 1;
+    A.rows_bound = std::min<int64_t>((int64_t)rows, (P + used * (kMAlign - 1) + kMAlign - 1) / kMAlign * kMAlign);
+    A.dh = (uint16_t*)ws;
+    A.dy1 = (uint16_t*)(ws + up(rows * I * 2, kAlign));
+    A.dxp = (uint16_t*)(ws + up(rows * I * 2, kAlign) + up(rows * 2 * I * 2, kAlign));
+    A.dx = dx;
+    A.dprobs = dprobs;
+    A.dw1 = dw1;
+    A.dw2 = dw2;
+    return hip_status(launch_moe_backward(A, (hipStream_t)stream));
+}
+
 int nvfp4moe_moe_expert_forward_w4a16(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids,
                                       const float* probs, const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q,
                                       uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {

@@ -1,0 +1,343 @@
+// backward.hip -- BF16 straight-through backward of the expert forward.
+//
+// miniTE summary page, "how it differs": the backward takes quantization as
+// the identity (straight-through) and runs BF16 GEMMs on the stored original
+// BF16 activations and weights, so nothing is quantized on the way back; the
+// router probability multiplies the SwiGLU output, and the combine is a plain
+// sum over the top-k slots.  With sorted row r holding pair p = t*K + k of
+// expert e (the forward's sort), the steps are
+//   dh[r]      = bf16(dout[t] . W2[e])                     grouped GEMM, K = H
+//   dgate, dup = bf16(dh p up silu'(gate)), bf16(dh p silu(gate))
+//   dprob[p]   = sum_n dh silu(gate) up                    FP32, one fixed order
+//   dxp[r]     = bf16([dgate | dup] . W1[e])               grouped GEMM, K = 2I
+//   dx[t]      = bf16(FP32 slot-order sum of dxp)          the forward's combine
+//   dW2[e]     = sum over e's rows of dout[t]^T h[r]       FP32, K = e's rows
+//   dW1[e]     = sum over e's rows of [dgate|dup]^T x[t]   FP32, K = e's rows
+// with gate, up the forward's BF16 FC1 output y1 and h its BF16 FC2 input.
+//
+// One GEMM kernel serves the four products: a workgroup of 4 wavefronts owns
+// a 128 x 128 output tile (each wave 64 x 64 = 2 x 2 MFMA tiles of
+// v_mfma_f32_32x32x16_bf16, FP32 accumulation) and walks K in chunks of 32
+// through LDS, where both operands are stored k-contiguous per output row or
+// column, the layout the MFMA fragments read.  An operand whose memory rows
+// run along k (the activations of dh and dxp) is copied 16 bytes at a time;
+// one whose rows run along the output index (the weights; both operands of
+// the weight gradients, whose k is the expert's rows) is transposed on the
+// way into LDS.  Rows are gathered through the forward's row -> pair map
+// where the operand is a token's row (dout, x).  Every output element is one
+// MFMA chain in increasing k: no split-K, so the results are deterministic,
+// and each row of dh, dxp and dx depends only on its own inputs.
+#include "nvfp4_device.h"
+#include "nvfp4_kernels.h"
+
+namespace nvfp4 {
+
+typedef __bf16 bf16x8b __attribute__((ext_vector_type(8)));
+
+constexpr int kBwdThreads = 256;
+constexpr int kBwdTile = 128;   // output rows and columns per workgroup
+constexpr int kBwdChunk = 32;   // k per LDS chunk (two MFMA k-steps)
+constexpr int kBwdPitch = kBwdChunk + 8;  // halves per LDS row (k-contiguous, padded)
+
+struct BwdShared {
+    uint16_t a[kBwdTile][kBwdPitch];
+    uint16_t b[kBwdTile][kBwdPitch];
+};
+
+// Row of an operand in memory: identity, or the token of a sorted row (through
+// row2pair; padding rows, -1, read token 0 and are never stored or are zero-filled).
+__device__ __forceinline__ int64_t bwd_row(int64_t r, bool gather, const int32_t* row2pair, int32_t K) {
+    if (!gather) return r;
+    const int32_t p = row2pair[r];
+    return p >= 0 ? (int64_t)((uint32_t)p / (uint32_t)K) : 0;
+}
+
+// Operand loader for one 32-deep chunk of a 128-wide operand tile into LDS
+// [index][k].  KC: memory row = output index (rows run along k); MC: memory
+// row = k (rows run along the output index).  Two 16-byte pieces per thread.
+template <bool KC>
+struct BwdLoad {
+    u32x4 v[2];
+    bool live[2];
+    __device__ __forceinline__ void fetch(const uint16_t* base, int64_t ld, bool gather, const int32_t* row2pair,
+                                          int32_t K, int64_t idx0, int64_t idx_end, int64_t k0, int64_t k_end) {
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int piece = threadIdx.x + h * kBwdThreads;
+            int64_t row, col;
+            if (KC) {  // 128 index rows x 4 pieces of 8 k
+                const int64_t i = idx0 + piece / 4;
+                live[h] = i < idx_end;
+                row = bwd_row(live[h] ? i : idx0, gather, row2pair, K);
+                col = k0 + 8 * (piece % 4);
+            } else {  // 32 k rows x 16 pieces of 8 indices
+                const int64_t k = k0 + piece / 16;
+                live[h] = k < k_end;
+                row = bwd_row(live[h] ? k : k0, gather, row2pair, K);
+                col = idx0 + 8 * (piece % 16);
+            }
+            v[h] = *reinterpret_cast<const u32x4*>(base + row * ld + col);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t (*lds)[kBwdPitch]) const {
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int piece = threadIdx.x + h * kBwdThreads;
+            const u32x4 w = live[h] ? v[h] : u32x4{0u, 0u, 0u, 0u};
+            if (KC) {
+                *reinterpret_cast<u32x4*>(&lds[piece / 4][8 * (piece % 4)]) = w;
+            } else {
+                const int k = piece / 16, i0 = 8 * (piece % 16);
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    lds[i0 + 2 * q][k] = (uint16_t)(w[q] & 0xFFFFu);
+                    lds[i0 + 2 * q + 1][k] = (uint16_t)(w[q] >> 16);
+                }
+            }
+        }
+    }
+};
+
+struct BwdGemmParams {
+    const uint16_t* a;
+    int64_t lda;
+    bool a_gather;
+    const uint16_t* b;
+    int64_t ldb;
+    int64_t b_estride;  // elements between experts' B matrices (weights), 0 for activations
+    bool b_gather;
+    const int32_t* row2pair;
+    int32_t top_k;
+    // cases by row tile (dh, dxp): tiles from the forward's row-tile table
+    const int4* mtiles;
+    const int32_t* n_mtiles;
+    // cases by expert (weight gradients): K = the expert's rows
+    const int32_t* expert_off;
+    const int32_t* expert_count;
+    int32_t M, N, Kd;
+    int32_t n_tiles_n, n_tiles_m;
+    void* out;
+    int64_t ldc;
+    int64_t c_estride;
+};
+
+// BY_EXPERT false: C[r][n] = sum_k A[r][k] B[k][n] over k < Kd for the rows r
+// of a row tile (A KC, BF16 output, rows past the expert's end not stored).
+// BY_EXPERT true: C_e[m][n] = sum over e's rows r of A[r][m] B[r][n] (A and B
+// MC, FP32 output).
+template <bool BY_EXPERT>
+__global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams P) {
+    __shared__ BwdShared S;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int64_t tile = blockIdx.x;
+    int64_t m0, m_end, n0, k_begin, k_end, expert, row_end = 0;
+    if (!BY_EXPERT) {
+        const int64_t mt = tile / P.n_tiles_n;
+        if (mt >= *P.n_mtiles) return;
+        const int4 d = P.mtiles[mt];
+        m0 = d.x;
+        m_end = d.x + 32 * d.z;
+        row_end = d.w;
+        expert = d.y;
+        n0 = (tile % P.n_tiles_n) * kBwdTile;
+        k_begin = 0;
+        k_end = P.Kd;
+    } else {
+        const int64_t per_e = (int64_t)P.n_tiles_m * P.n_tiles_n;
+        expert = tile / per_e;
+        const int64_t rem = tile % per_e;
+        m0 = (rem / P.n_tiles_n) * kBwdTile;
+        m_end = P.M;
+        n0 = (rem % P.n_tiles_n) * kBwdTile;
+        k_begin = P.expert_off[expert];
+        k_end = k_begin + P.expert_count[expert];
+    }
+    const uint16_t* bbase = P.b + expert * P.b_estride;
+    BwdLoad<!BY_EXPERT> la;
+    BwdLoad<false> lb;
+    // A: BY_EXPERT false, KC with memory rows m (sorted rows); true, MC with
+    // memory rows k (sorted rows).  B: MC with memory rows k -- an expert's
+    // weight rows, or sorted rows.
+    auto fetch = [&](int64_t k0) {
+        la.fetch(P.a, P.lda, P.a_gather, P.row2pair, P.top_k, m0, m_end, k0, k_end);
+        lb.fetch(bbase, P.ldb, P.b_gather, P.row2pair, P.top_k, n0, P.N, k0, k_end);
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) acc[i][j] = f32x16{};
+    const int r = lane & 31, kh = lane >> 5;
+    if (k_begin < k_end) fetch(k_begin);
+    for (int64_t k0 = k_begin; k0 < k_end; k0 += kBwdChunk) {
+        __syncthreads();  // the previous chunk's fragments are read
+        la.store(S.a);
+        lb.store(S.b);
+        __syncthreads();
+        if (k0 + kBwdChunk < k_end) fetch(k0 + kBwdChunk);  // next chunk in flight during the MFMAs
+#pragma unroll
+        for (int ks = 0; ks < kBwdChunk / 16; ks++) {
+            bf16x8b af[2], bfr[2];
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+                af[i] = __builtin_bit_cast(bf16x8b, *reinterpret_cast<const u32x4*>(&S.a[64 * wm + 32 * i + r][16 * ks + 8 * kh]));
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                bfr[j] = __builtin_bit_cast(bf16x8b, *reinterpret_cast<const u32x4*>(&S.b[64 * wn + 32 * j + r][16 * ks + 8 * kh]));
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    // register q of tile (i, j): row 64 wm + 32 i + (q/4)*8 + kh*4 + q%4, column 64 wn + 32 j + r
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int q = 0; q < 16; q++) {
+                const int64_t row = m0 + 64 * wm + 32 * i + (q >> 2) * 8 + kh * 4 + (q & 3);
+                const int64_t col = n0 + 64 * wn + 32 * j + r;
+                if (!BY_EXPERT) {
+                    if (row < row_end && row < m_end)
+                        reinterpret_cast<uint16_t*>(P.out)[row * P.ldc + col] = (uint16_t)bf16_hw(acc[i][j][q]);
+                } else if (row < m_end) {
+                    reinterpret_cast<float*>(P.out)[expert * P.c_estride + row * P.ldc + col] = acc[i][j][q];
+                }
+            }
+}
+
+// SwiGLU backward per sorted row holding a pair (one wavefront per row):
+// dgate = bf16(((dh p) up) silu'(gate)), dup = bf16((dh p) silu(gate)),
+// dprob = FP32 sum of dh silu(gate) up, each lane over its columns in
+// increasing order, then a fixed butterfly.  silu and silu' use the hardware
+// exp2 and reciprocal: sig = 1 / (1 + e^-g), silu = g sig,
+// silu' = sig (1 + g (1 - sig)).
+__global__ void __launch_bounds__(256) swiglu_backward_kernel(const uint16_t* __restrict__ dh,
+                                                              const uint16_t* __restrict__ y1, int64_t rows,
+                                                              int32_t I, const int32_t* __restrict__ row2pair,
+                                                              const float* __restrict__ row_prob,
+                                                              const int32_t* __restrict__ expert_off, int32_t E,
+                                                              uint16_t* __restrict__ dy1, float* __restrict__ dprobs) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows || r >= expert_off[E]) return;
+    const int32_t p = row2pair[r];
+    if (p < 0) return;
+    const float pr = row_prob[r];
+    float dp = 0.0f;
+    for (int n = lane; n < I; n += kWave) {
+        const float d = bf16_to_f32(dh[r * I + n]);
+        const float g = bf16_to_f32(y1[r * 2 * I + n]);
+        const float u = bf16_to_f32(y1[r * 2 * I + I + n]);
+        const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+        const float s = g * sig;
+        const float ds = sig * (1.0f + g * (1.0f - sig));
+        const float dpr = d * pr;
+        dy1[r * 2 * I + n] = (uint16_t)bf16_hw(dpr * u * ds);
+        dy1[r * 2 * I + I + n] = (uint16_t)bf16_hw(dpr * s);
+        dp = dp + d * s * u;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) dp += __shfl_xor(dp, o, kWave);
+    if (lane == 0) dprobs[p] = dp;
+}
+
+hipError_t launch_bwd_gemm(bool by_expert, const BwdGemmParams& P, int64_t tiles, hipStream_t stream) {
+    if (tiles <= 0) return hipSuccess;
+    if (by_expert)
+        hipLaunchKernelGGL(bwd_gemm_kernel<true>, dim3((unsigned)tiles), dim3(kBwdThreads), 0, stream, P);
+    else
+        hipLaunchKernelGGL(bwd_gemm_kernel<false>, dim3((unsigned)tiles), dim3(kBwdThreads), 0, stream, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_backward(const BwdArgs& A, hipStream_t stream) {
+    const int64_t E = A.E, H = A.H, I = A.I;
+    // dh = dout (gathered) . W2[e]: A KC (rows of dout, through row2pair), B MC (W2[e] rows: k = m).
+    BwdGemmParams g{};
+    g.row2pair = A.row2pair;
+    g.top_k = A.top_k;
+    g.mtiles = A.mtiles;
+    g.n_mtiles = A.n_mtiles;
+    g.expert_off = A.expert_off;
+    g.expert_count = A.expert_count;
+    g.a = A.dout;
+    g.lda = H;
+    g.a_gather = true;
+    g.b = A.w2;
+    g.ldb = I;
+    g.b_estride = H * I;
+    g.b_gather = false;
+    g.N = (int32_t)I;
+    g.Kd = (int32_t)H;
+    g.n_tiles_n = (int32_t)(I / kBwdTile);
+    g.out = A.dh;
+    g.ldc = I;
+    hipError_t e = launch_bwd_gemm(false, g, A.mt_bound * g.n_tiles_n, stream);
+    if (e != hipSuccess) return e;
+    // the SwiGLU backward and the router-probability gradient
+    hipLaunchKernelGGL(swiglu_backward_kernel, dim3((unsigned)((A.rows_bound + 3) / 4)), dim3(256), 0, stream, A.dh,
+                       A.y1, A.rows_bound, (int32_t)I, A.row2pair, A.row_prob, A.expert_off, (int32_t)E, A.dy1,
+                       A.dprobs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // dxp = dy1 . W1[e]: A KC (dy1 rows), B MC (W1[e] rows: k = j)
+    BwdGemmParams x1 = g;
+    x1.a = A.dy1;
+    x1.lda = 2 * I;
+    x1.a_gather = false;
+    x1.b = A.w1;
+    x1.ldb = H;
+    x1.b_estride = 2 * I * H;
+    x1.N = (int32_t)H;
+    x1.Kd = (int32_t)(2 * I);
+    x1.n_tiles_n = (int32_t)(H / kBwdTile);
+    x1.out = A.dxp;
+    x1.ldc = H;
+    e = launch_bwd_gemm(false, x1, A.mt_bound * x1.n_tiles_n, stream);
+    if (e != hipSuccess) return e;
+    // dW2[e] = dout(rows of e)^T h(rows of e): A MC (dout rows, gathered), B MC (h rows)
+    BwdGemmParams w2 = g;
+    w2.a = A.dout;
+    w2.lda = H;
+    w2.a_gather = true;
+    w2.b = A.h;
+    w2.ldb = I;
+    w2.b_estride = 0;
+    w2.b_gather = false;
+    w2.M = (int32_t)H;
+    w2.N = (int32_t)I;
+    w2.n_tiles_m = (int32_t)(H / kBwdTile);
+    w2.n_tiles_n = (int32_t)(I / kBwdTile);
+    w2.out = A.dw2;
+    w2.ldc = I;
+    w2.c_estride = H * I;
+    e = launch_bwd_gemm(true, w2, E * w2.n_tiles_m * w2.n_tiles_n, stream);
+    if (e != hipSuccess) return e;
+    // dW1[e] = dy1(rows of e)^T x(rows of e): A MC (dy1 rows), B MC (x rows, gathered)
+    BwdGemmParams w1 = g;
+    w1.a = A.dy1;
+    w1.lda = 2 * I;
+    w1.a_gather = false;
+    w1.b = A.x;
+    w1.ldb = H;
+    w1.b_estride = 0;
+    w1.b_gather = true;
+    w1.M = (int32_t)(2 * I);
+    w1.N = (int32_t)H;
+    w1.n_tiles_m = (int32_t)(2 * I / kBwdTile);
+    w1.n_tiles_n = (int32_t)(H / kBwdTile);
+    w1.out = A.dw1;
+    w1.ldc = H;
+    w1.c_estride = 2 * I * H;
+    e = launch_bwd_gemm(true, w1, E * w1.n_tiles_m * w1.n_tiles_n, stream);
+    if (e != hipSuccess) return e;
+    // dx = FP32 slot-order sum of each token's dxp rows (the forward's combine)
+    return launch_combine(A.dxp, A.pair2row, A.T, (int32_t)H, A.top_k, A.dx, stream);
+}
+
+}  // namespace nvfp4

@@ -109,6 +109,35 @@ __device__ __forceinline__ bool row_tile_used(int64_t rt, int32_t E, int32_t cap
     return r - e * capacity < (kept + kMAlign - 1) / kMAlign * kMAlign;
 }
 #endif
+// The BF16 straight-through backward (backward.hip): buffers from the
+// forward (sort metadata, row probabilities, h, y1) and its own.
+struct BwdArgs {
+    int32_t T, top_k;
+    int64_t E, H, I;
+    const uint16_t* x;       // [T, H]
+    const uint16_t* w1;      // [E, 2I, H] BF16
+    const uint16_t* w2;      // [E, H, I] BF16
+    const uint16_t* y1;      // [rows, 2I] the forward's FC1 output per sorted row
+    const uint16_t* h;       // [rows, I] the forward's FC2 input per sorted row
+    const uint16_t* dout;    // [T, H]
+    const int32_t* row2pair;
+    const int32_t* pair2row;
+    const float* row_prob;
+    const int4* mtiles;
+    const int32_t* n_mtiles;
+    const int32_t* expert_off;
+    const int32_t* expert_count;
+    int64_t mt_bound, rows_bound;
+    uint16_t* dh;            // [rows, I]
+    uint16_t* dy1;           // [rows, 2I]
+    uint16_t* dxp;           // [rows, H]
+    uint16_t* dx;            // [T, H]
+    float* dprobs;           // [T, K]
+    float* dw1;              // [E, 2I, H]
+    float* dw2;              // [E, H, I]
+};
+hipError_t launch_moe_backward(const BwdArgs& args, hipStream_t stream);
+
 int gemm_cols_per_tile(int mode);  // output columns per tile: 256 (plain) or 128 of h (128 gate + 128 up rows)
 hipError_t launch_gemm(int mode, const GemmParams& P, int grid_blocks, hipStream_t stream);
 // The router-weighted SwiGLU producer on its own (unfused forward): h and the
