@@ -13,8 +13,8 @@ forwards right after the timed region; the CPU oracle is timed on a bounded
 sample on the host cores.
 
 The secondary measurements (weight quantization, cold-cache forwards, the
-dense linear, the skewed and W4A16 workloads, the masked layout, the router,
-decode sizes) run before the headline forwards.  They also bring the GPU
+dense linear, the skewed and W4A16 workloads, the masked layout, the BF16
+backward, the router, decode sizes) run before the headline forwards.  They also bring the GPU
 from idle to its steady clocks, which takes about 80 back-to-back forwards,
 so the W warm-up steps and the K timed steps see the clocks of a layer that
 runs continuously, whatever W is.
@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--no-skewed", action="store_true", help="skip the skewed-routing T = 16384 forwards")
     ap.add_argument("--no-router", action="store_true", help="skip the on-device router (scores + top-k)")
     ap.add_argument("--no-masked", action="store_true", help="skip the masked fixed-capacity forward")
+    ap.add_argument("--no-backward", action="store_true", help="skip the BF16 straight-through backward")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -319,6 +320,35 @@ def main():
                   "what": "same workload, expert rows in fixed chunks of `capacity` (static-capacity layout)"}
         del ws_m
 
+    # The BF16 straight-through backward (secondary): after the unfused forward
+    # that stores y1, the backward of the same layer with a random upstream
+    # gradient; dh, each pair's FC1 input gradient and both weight gradients
+    # are 2 * T*K * 6 * H * I flop in BF16 MFMA.
+    backward = None
+    if not args.no_backward:
+        w1_b = torch.from_numpy(w1.view(np.int16)).to(dev)
+        w2_b = torch.from_numpy(w2.view(np.int16)).to(dev)
+        out_u, y1_u = m.moe_expert_forward_unfused(cfg, x, ids, probs, qw, ws)
+        rng = np.random.default_rng(32)
+        dout = torch.from_numpy(W.f32_to_bf16_bits((rng.standard_normal((T, H)) * 0.1).astype(np.float32))
+                                .view(np.int16)).to(dev)
+        for _ in range(3):
+            m.moe_expert_backward(cfg, x, w1_b, w2_b, y1_u, ws, dout)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        n_b = 10
+        ev[0].record(stream)
+        for _ in range(n_b):
+            m.moe_expert_backward(cfg, x, w1_b, w2_b, y1_u, ws, dout, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        b_ms = ev[0].elapsed_time(ev[1]) / n_b
+        b_flop = 2.0 * T * K * 6 * H * I
+        backward = {"ms": b_ms, "tflops": b_flop / (b_ms / 1e3) / 1e12,
+                    "frac_bf16_mfma_peak": b_flop / (b_ms / 1e3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                    "what": "dx, router-probability and FP32 weight gradients; each call allocates its "
+                            "outputs and workspace through torch (included)"}
+        del w1_b, w2_b, out_u, y1_u, dout
+
     # The on-device router (secondary): FP32 scores of x against a [E, H] BF16
     # router weight (N(0, 0.02^2), seed 21) and the deterministic top-k with
     # renormalised probabilities, for the whole batch and at decode sizes.
@@ -459,6 +489,8 @@ def main():
         result["masked"] = masked
     if router:
         result["router"] = router
+    if backward:
+        result["backward"] = backward
     if w16:
         result["w4a16"] = w16
     if dense:

@@ -17,13 +17,13 @@
 //
 // One GEMM kernel serves the four products: a workgroup of 4 wavefronts owns
 // a 128 x 128 output tile (each wave 64 x 64 = 2 x 2 MFMA tiles of
-// v_mfma_f32_32x32x16_bf16, FP32 accumulation) and walks K in chunks of 32
-// through LDS, where both operands are stored k-contiguous per output row or
-// column, the layout the MFMA fragments read.  An operand whose memory rows
-// run along k (the activations of dh and dxp) is copied 16 bytes at a time;
-// one whose rows run along the output index (the weights; both operands of
-// the weight gradients, whose k is the expert's rows) is transposed on the
-// way into LDS.  Rows are gathered through the forward's row -> pair map
+// v_mfma_f32_32x32x16_bf16, FP32 accumulation) and walks K in chunks of 64
+// through LDS, each operand staged as memory gives it (16-byte stores).  An
+// operand whose memory rows run along k (the activations of dh and dxp) gives
+// each MFMA fragment in one 16-byte LDS read; one whose rows run along the
+// output index (the weights; both operands of the weight gradients, whose k
+// is the expert's rows) is transposed by the fragment reads, eight 2-byte
+// reads down an LDS column.  Rows are gathered through the forward's row -> pair map
 // where the operand is a token's row (dout, x).  Every output element is one
 // MFMA chain in increasing k: no split-K, so the results are deterministic,
 // and each row of dh, dxp and dx depends only on its own inputs.
@@ -36,13 +36,11 @@ typedef __bf16 bf16x8b __attribute__((ext_vector_type(8)));
 
 constexpr int kBwdThreads = 256;
 constexpr int kBwdTile = 128;   // output rows and columns per workgroup
-constexpr int kBwdChunk = 32;   // k per LDS chunk (two MFMA k-steps)
-constexpr int kBwdPitch = kBwdChunk + 8;  // halves per LDS row (k-contiguous, padded)
-
-struct BwdShared {
-    uint16_t a[kBwdTile][kBwdPitch];
-    uint16_t b[kBwdTile][kBwdPitch];
-};
+constexpr int kBwdChunk = 64;   // k per LDS chunk (four MFMA k-steps)
+constexpr int kKcPitch = kBwdChunk + 8;  // halves per LDS row of a KC operand, [index][k]
+constexpr int kMcPitch = kBwdTile + 8;   // halves per LDS row of an MC operand, [k][index]
+constexpr int kBwdPieces = kBwdTile * kBwdChunk / 8 / kBwdThreads;  // 16-byte pieces per thread and operand
+constexpr int kBwdOperandLds = (kBwdTile * kKcPitch > kBwdChunk * kMcPitch ? kBwdTile * kKcPitch : kBwdChunk * kMcPitch);
 
 // Row of an operand in memory: identity, or the token of a sorted row (through
 // row2pair; padding rows, -1, read token 0 and are never stored or are zero-filled).
@@ -52,49 +50,54 @@ __device__ __forceinline__ int64_t bwd_row(int64_t r, bool gather, const int32_t
     return p >= 0 ? (int64_t)((uint32_t)p / (uint32_t)K) : 0;
 }
 
-// Operand loader for one 32-deep chunk of a 128-wide operand tile into LDS
-// [index][k].  KC: memory row = output index (rows run along k); MC: memory
-// row = k (rows run along the output index).  Two 16-byte pieces per thread.
+// One 64-deep chunk of a 128-wide operand tile, staged in LDS as memory gives
+// it, 16 bytes per store.  KC (memory rows run along k): LDS [index][k], and
+// an MFMA fragment (8 consecutive k of one index) is one 16-byte read.  MC
+// (memory rows run along the index): LDS [k][index], and a fragment is eight
+// 2-byte reads down a column (a wave's 32 indices of one k are 64 contiguous
+// bytes, so the reads are conflict-free).
 template <bool KC>
 struct BwdLoad {
-    u32x4 v[2];
-    bool live[2];
+    u32x4 v[kBwdPieces];
+    bool live[kBwdPieces];
     __device__ __forceinline__ void fetch(const uint16_t* base, int64_t ld, bool gather, const int32_t* row2pair,
                                           int32_t K, int64_t idx0, int64_t idx_end, int64_t k0, int64_t k_end) {
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
+        for (int h = 0; h < kBwdPieces; h++) {
             const int piece = threadIdx.x + h * kBwdThreads;
             int64_t row, col;
-            if (KC) {  // 128 index rows x 4 pieces of 8 k
-                const int64_t i = idx0 + piece / 4;
+            if (KC) {  // 128 index rows x 8 pieces of 8 k
+                const int64_t i = idx0 + piece / (kBwdChunk / 8);
                 live[h] = i < idx_end;
                 row = bwd_row(live[h] ? i : idx0, gather, row2pair, K);
-                col = k0 + 8 * (piece % 4);
-            } else {  // 32 k rows x 16 pieces of 8 indices
-                const int64_t k = k0 + piece / 16;
+                col = k0 + 8 * (piece % (kBwdChunk / 8));
+            } else {  // 64 k rows x 16 pieces of 8 indices
+                const int64_t k = k0 + piece / (kBwdTile / 8);
                 live[h] = k < k_end;
                 row = bwd_row(live[h] ? k : k0, gather, row2pair, K);
-                col = idx0 + 8 * (piece % 16);
+                col = idx0 + 8 * (piece % (kBwdTile / 8));
             }
             v[h] = *reinterpret_cast<const u32x4*>(base + row * ld + col);
         }
     }
-    __device__ __forceinline__ void store(uint16_t (*lds)[kBwdPitch]) const {
+    __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
+        for (int h = 0; h < kBwdPieces; h++) {
             const int piece = threadIdx.x + h * kBwdThreads;
             const u32x4 w = live[h] ? v[h] : u32x4{0u, 0u, 0u, 0u};
-            if (KC) {
-                *reinterpret_cast<u32x4*>(&lds[piece / 4][8 * (piece % 4)]) = w;
-            } else {
-                const int k = piece / 16, i0 = 8 * (piece % 16);
-#pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    lds[i0 + 2 * q][k] = (uint16_t)(w[q] & 0xFFFFu);
-                    lds[i0 + 2 * q + 1][k] = (uint16_t)(w[q] >> 16);
-                }
-            }
+            const int at = KC ? (piece / (kBwdChunk / 8)) * kKcPitch + 8 * (piece % (kBwdChunk / 8))
+                              : (piece / (kBwdTile / 8)) * kMcPitch + 8 * (piece % (kBwdTile / 8));
+            *reinterpret_cast<u32x4*>(lds + at) = w;
         }
+    }
+    // Fragment: k = kb .. kb + 7 of index idx.
+    __device__ __forceinline__ bf16x8b frag(const uint16_t* lds, int idx, int kb) const {
+        if (KC) return __builtin_bit_cast(bf16x8b, *reinterpret_cast<const u32x4*>(lds + idx * kKcPitch + kb));
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            w[q] = (uint32_t)lds[(kb + 2 * q) * kMcPitch + idx] | ((uint32_t)lds[(kb + 2 * q + 1) * kMcPitch + idx] << 16);
+        return __builtin_bit_cast(bf16x8b, w);
     }
 };
 
@@ -127,7 +130,8 @@ struct BwdGemmParams {
 // MC, FP32 output).
 template <bool BY_EXPERT>
 __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams P) {
-    __shared__ BwdShared S;
+    __shared__ __attribute__((aligned(16))) uint16_t SA[kBwdOperandLds];
+    __shared__ __attribute__((aligned(16))) uint16_t SB[kBwdOperandLds];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
     const int64_t tile = blockIdx.x;
@@ -172,19 +176,17 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
     if (k_begin < k_end) fetch(k_begin);
     for (int64_t k0 = k_begin; k0 < k_end; k0 += kBwdChunk) {
         __syncthreads();  // the previous chunk's fragments are read
-        la.store(S.a);
-        lb.store(S.b);
+        la.store(SA);
+        lb.store(SB);
         __syncthreads();
         if (k0 + kBwdChunk < k_end) fetch(k0 + kBwdChunk);  // next chunk in flight during the MFMAs
 #pragma unroll
         for (int ks = 0; ks < kBwdChunk / 16; ks++) {
             bf16x8b af[2], bfr[2];
 #pragma unroll
-            for (int i = 0; i < 2; i++)
-                af[i] = __builtin_bit_cast(bf16x8b, *reinterpret_cast<const u32x4*>(&S.a[64 * wm + 32 * i + r][16 * ks + 8 * kh]));
+            for (int i = 0; i < 2; i++) af[i] = la.frag(SA, 64 * wm + 32 * i + r, 16 * ks + 8 * kh);
 #pragma unroll
-            for (int j = 0; j < 2; j++)
-                bfr[j] = __builtin_bit_cast(bf16x8b, *reinterpret_cast<const u32x4*>(&S.b[64 * wn + 32 * j + r][16 * ks + 8 * kh]));
+            for (int j = 0; j < 2; j++) bfr[j] = lb.frag(SB, 64 * wn + 32 * j + r, 16 * ks + 8 * kh);
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
