@@ -22,8 +22,8 @@
 // operand whose memory rows run along k (the activations of dh and dxp) gives
 // each MFMA fragment in one 16-byte LDS read; one whose rows run along the
 // output index (the weights; both operands of the weight gradients, whose k
-// is the expert's rows) is transposed by the fragment reads, eight 2-byte
-// reads down an LDS column.  Rows are gathered through the forward's row -> pair map
+// is the expert's rows) is transposed by the fragment reads (the LDS
+// transpose read ds_read_b64_tr_b16).  Rows are gathered through the forward's row -> pair map
 // where the operand is a token's row (dout, x).  Every output element is one
 // MFMA chain in increasing k: no split-K, so the results are deterministic,
 // and each row of dh, dxp and dx depends only on its own inputs.
@@ -53,9 +53,8 @@ __device__ __forceinline__ int64_t bwd_row(int64_t r, bool gather, const int32_t
 // One 64-deep chunk of a 128-wide operand tile, staged in LDS as memory gives
 // it, 16 bytes per store.  KC (memory rows run along k): LDS [index][k], and
 // an MFMA fragment (8 consecutive k of one index) is one 16-byte read.  MC
-// (memory rows run along the index): LDS [k][index], and a fragment is eight
-// 2-byte reads down a column (a wave's 32 indices of one k are 64 contiguous
-// bytes, so the reads are conflict-free).
+// (memory rows run along the index): LDS [k][index], and a fragment is two
+// transposing 8-byte reads.
 template <bool KC>
 struct BwdLoad {
     u32x4 v[kBwdPieces];
@@ -90,14 +89,29 @@ struct BwdLoad {
             *reinterpret_cast<u32x4*>(lds + at) = w;
         }
     }
-    // Fragment: k = kb .. kb + 7 of index idx.
-    __device__ __forceinline__ bf16x8b frag(const uint16_t* lds, int idx, int kb) const {
-        if (KC) return __builtin_bit_cast(bf16x8b, *reinterpret_cast<const u32x4*>(lds + idx * kKcPitch + kb));
-        u32x4 w;
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-            w[q] = (uint32_t)lds[(kb + 2 * q) * kMcPitch + idx] | ((uint32_t)lds[(kb + 2 * q + 1) * kMcPitch + idx] << 16);
-        return __builtin_bit_cast(bf16x8b, w);
+    // MFMA fragment of the 32 indices [base, base + 32) at k = kb .. kb + 15:
+    // lane (kh*32 + c) gets k = kb + 8 kh .. kb + 8 kh + 7 of index base + c.
+    // MC uses the LDS transpose read ds_read_b64_tr_b16: within each group of
+    // 16 lanes, source lane s reads 4 consecutive halves and output lane L
+    // receives half L % 4 of source lanes L / 4, 4 + L / 4, 8 + L / 4 and
+    // 12 + L / 4 (checked on the GPU by reading an index-filled array), so
+    // source lane s reads row k0 + s / 4 at indices 4 (s % 4) .. + 3 of the
+    // group's 16 and each output lane gets 4 consecutive k of one index; two
+    // reads give the 8.
+    __device__ __forceinline__ bf16x8b frag(uint16_t* lds, int base, int kb) const {
+        const int lane = threadIdx.x & 63;
+        if (KC)
+            return __builtin_bit_cast(
+                bf16x8b, *reinterpret_cast<const u32x4*>(lds + (base + (lane & 31)) * kKcPitch + kb + 8 * (lane >> 5)));
+        const int g = lane >> 4, sl = lane & 15;
+        const int row = kb + 8 * (g >> 1) + (sl >> 2), col = base + 16 * (g & 1) + 4 * (sl & 3);
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(lds + row * kMcPitch + col));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(lds + (row + 4) * kMcPitch + col));
+        const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+        return __builtin_bit_cast(bf16x8b, u32x4{a[0], a[1], b[0], b[1]});
     }
 };
 
@@ -184,9 +198,9 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
         for (int ks = 0; ks < kBwdChunk / 16; ks++) {
             bf16x8b af[2], bfr[2];
 #pragma unroll
-            for (int i = 0; i < 2; i++) af[i] = la.frag(SA, 64 * wm + 32 * i + r, 16 * ks + 8 * kh);
+            for (int i = 0; i < 2; i++) af[i] = la.frag(SA, 64 * wm + 32 * i, 16 * ks);
 #pragma unroll
-            for (int j = 0; j < 2; j++) bfr[j] = lb.frag(SB, 64 * wn + 32 * j + r, 16 * ks + 8 * kh);
+            for (int j = 0; j < 2; j++) bfr[j] = lb.frag(SB, 64 * wn + 32 * j, 16 * ks);
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
