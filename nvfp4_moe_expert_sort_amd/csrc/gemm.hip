@@ -347,33 +347,49 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
         }
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_wave_barrier();
-        const int32_t hc = bcol0[0];
-        const int32_t part = hc >> 5;
+        const int32_t part = bcol0[0] >> 5;
 #pragma unroll
         for (int half = 0; half < 2; half++) {
             const int rl = lane + 64 * half;
             if (rl < 32 * NSUB) {
                 const u32x4* src = reinterpret_cast<const u32x4*>(E + rl * kPitch);
-                u32x4 v[4];
                 u16x2 m = {0, 0};
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
-                    v[q] = src[q];
+                    const u32x4 v = src[q];
 #pragma unroll
                     for (int j = 0; j < 4; j++)
-                        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v[q][j] & 0x7FFF7FFFu));
+                        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v[j] & 0x7FFF7FFFu));
                 }
                 const int32_t row = row0 + rl;
                 if (row < row_end) {
-                    u32x4* dst = reinterpret_cast<u32x4*>(P.out + (int64_t)row * P.ld_out + hc);
-#pragma unroll
-                    for (int q = 0; q < 4; q++) dst[q] = v[q];
                     // max |h| over these 32 columns: BF16 bit patterns of |h|
                     // order like their values, so the integer max is exact.
                     const uint32_t mb = max((uint32_t)m[0], (uint32_t)m[1]);
                     P.amax_part[(int64_t)row * P.n_part + part] = __uint_as_float(mb << 16);
                 }
             }
+        }
+        // h leaves in whole 128-byte lines: once all four waves have staged
+        // their 32 columns, the workgroup stores its 128 columns (256 bytes
+        // of each row), 16 lanes per row, 16-byte chunk c of row r going to
+        // thread (16 r + c) % 256.  (All four waves reach this barrier: the
+        // inner size is a multiple of 128, so every wave has h columns.)
+        barrier_lds();
+        // (the thread index passes through an empty asm after the barrier, so
+        // the store addresses are not computed before the K loop and held
+        // in registers across it)
+        int tid = (int)threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const uint16_t* E0 = reinterpret_cast<const uint16_t*>(&S);
+        const int32_t hc0 = nt * 128;
+#pragma unroll
+        for (int q = 0; q < 2 * NSUB; q++) {
+            const int c = q * kThreads + tid;
+            const int rl = c >> 4, cc = c & 15;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(E0 + (cc >> 2) * (128 * kPitch) + rl * kPitch + 8 * (cc & 3));
+            const int32_t row = row0 + rl;
+            if (row < row_end) *reinterpret_cast<u32x4*>(P.out + (int64_t)row * P.ld_out + hc0 + 8 * cc) = v;
         }
     } else {
         constexpr int kPitch = 72;  // halves per staged row: 64 columns + 8 pad (144 B, conflict-free)
