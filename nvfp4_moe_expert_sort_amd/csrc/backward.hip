@@ -133,6 +133,7 @@ struct BwdGemmParams {
     const int32_t* expert_count;
     int32_t M, N, Kd;
     int32_t n_tiles_n, n_tiles_m;
+    int64_t n_tiles;  // cases by expert: E * n_tiles_m * n_tiles_n (by row tile: read on the device)
     void* out;
     int64_t ldc;
     int64_t c_estride;
@@ -148,11 +149,20 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
     __shared__ __attribute__((aligned(16))) uint16_t SB[kBwdOperandLds];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
-    const int64_t tile = blockIdx.x;
+    // Workgroup b runs on XCD b % 8 (round-robin dispatch), and XCD x takes
+    // the contiguous range [x * span, (x + 1) * span) of the tile list, in
+    // which tiles that share an expert's operands (its weights, or its rows of
+    // the activations) are neighbours: they meet in that XCD's L2 instead of
+    // being fetched by all eight.  The grid is a multiple of 8 covering
+    // 8 * span workgroups.
+    const int64_t total = BY_EXPERT ? P.n_tiles : (int64_t)(*P.n_mtiles) * P.n_tiles_n;
+    const int64_t span = (total + 7) / 8, slot = blockIdx.x >> 3;
+    if (slot >= span) return;
+    const int64_t tile = (int64_t)(blockIdx.x & 7) * span + slot;
+    if (tile >= total) return;
     int64_t m0, m_end, n0, k_begin, k_end, expert, row_end = 0;
     if (!BY_EXPERT) {
         const int64_t mt = tile / P.n_tiles_n;
-        if (mt >= *P.n_mtiles) return;
         const int4 d = P.mtiles[mt];
         m0 = d.x;
         m_end = d.x + 32 * d.z;
@@ -264,10 +274,14 @@ __global__ void __launch_bounds__(256) swiglu_backward_kernel(const uint16_t* __
 
 hipError_t launch_bwd_gemm(bool by_expert, const BwdGemmParams& P, int64_t tiles, hipStream_t stream) {
     if (tiles <= 0) return hipSuccess;
-    if (by_expert)
-        hipLaunchKernelGGL(bwd_gemm_kernel<true>, dim3((unsigned)tiles), dim3(kBwdThreads), 0, stream, P);
-    else
-        hipLaunchKernelGGL(bwd_gemm_kernel<false>, dim3((unsigned)tiles), dim3(kBwdThreads), 0, stream, P);
+    const unsigned grid = (unsigned)((tiles + 7) / 8 * 8);  // XCD ranges of ceil(tiles / 8)
+    if (by_expert) {
+        BwdGemmParams Q = P;
+        Q.n_tiles = tiles;
+        hipLaunchKernelGGL(bwd_gemm_kernel<true>, dim3(grid), dim3(kBwdThreads), 0, stream, Q);
+    } else {
+        hipLaunchKernelGGL(bwd_gemm_kernel<false>, dim3(grid), dim3(kBwdThreads), 0, stream, P);
+    }
     return hipGetLastError();
 }
 
