@@ -59,24 +59,39 @@ template <bool KC>
 struct BwdLoad {
     u32x4 v[kBwdPieces];
     bool live[kBwdPieces];
-    __device__ __forceinline__ void fetch(const uint16_t* base, int64_t ld, bool gather, const int32_t* row2pair,
-                                          int32_t K, int64_t idx0, int64_t idx_end, int64_t k0, int64_t k_end) {
+    // Memory rows of this thread's pieces: KC, the tile's index rows (the same
+    // for every chunk, looked up once per tile); MC, the k rows of a chunk.
+    int32_t mrow[kBwdPieces];  // memory row indices are < 2^31
+    __device__ __forceinline__ void rows(bool gather, const int32_t* row2pair, int32_t K, int64_t idx0,
+                                         int64_t idx_end, int64_t k0, int64_t k_end) {
 #pragma unroll
         for (int h = 0; h < kBwdPieces; h++) {
             const int piece = threadIdx.x + h * kBwdThreads;
-            int64_t row, col;
             if (KC) {  // 128 index rows x 8 pieces of 8 k
                 const int64_t i = idx0 + piece / (kBwdChunk / 8);
-                live[h] = i < idx_end;
-                row = bwd_row(live[h] ? i : idx0, gather, row2pair, K);
-                col = k0 + 8 * (piece % (kBwdChunk / 8));
+                mrow[h] = (int32_t)bwd_row(i < idx_end ? i : idx0, gather, row2pair, K);
             } else {  // 64 k rows x 16 pieces of 8 indices
                 const int64_t k = k0 + piece / (kBwdTile / 8);
-                live[h] = k < k_end;
-                row = bwd_row(live[h] ? k : k0, gather, row2pair, K);
+                // rows past the end (or of an empty range) look up an in-bounds row; never used
+                const int64_t kk = k < k_end ? k : k_end - 1;
+                mrow[h] = (int32_t)bwd_row(kk > 0 ? kk : 0, gather, row2pair, K);
+            }
+        }
+    }
+    __device__ __forceinline__ void fetch(const uint16_t* base, int64_t ld, int64_t idx0, int64_t idx_end, int64_t k0,
+                                          int64_t k_end) {
+#pragma unroll
+        for (int h = 0; h < kBwdPieces; h++) {
+            const int piece = threadIdx.x + h * kBwdThreads;
+            int64_t col;
+            if (KC) {
+                live[h] = idx0 + piece / (kBwdChunk / 8) < idx_end;
+                col = k0 + 8 * (piece % (kBwdChunk / 8));
+            } else {
+                live[h] = k0 + piece / (kBwdTile / 8) < k_end;
                 col = idx0 + 8 * (piece % (kBwdTile / 8));
             }
-            v[h] = *reinterpret_cast<const u32x4*>(base + row * ld + col);
+            v[h] = *reinterpret_cast<const u32x4*>(base + (int64_t)mrow[h] * ld + col);
         }
     }
     __device__ __forceinline__ void store(uint16_t* lds) const {
@@ -187,9 +202,13 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
     // A: BY_EXPERT false, KC with memory rows m (sorted rows); true, MC with
     // memory rows k (sorted rows).  B: MC with memory rows k -- an expert's
     // weight rows, or sorted rows.
+    // fetch chunk k0: an MC operand looks up the chunk's rows first (a KC
+    // operand's rows are the tile's, looked up once)
     auto fetch = [&](int64_t k0) {
-        la.fetch(P.a, P.lda, P.a_gather, P.row2pair, P.top_k, m0, m_end, k0, k_end);
-        lb.fetch(bbase, P.ldb, P.b_gather, P.row2pair, P.top_k, n0, P.N, k0, k_end);
+        if (BY_EXPERT) la.rows(P.a_gather, P.row2pair, P.top_k, m0, m_end, k0, k_end);
+        lb.rows(P.b_gather, P.row2pair, P.top_k, n0, P.N, k0, k_end);
+        la.fetch(P.a, P.lda, m0, m_end, k0, k_end);
+        lb.fetch(bbase, P.ldb, n0, P.N, k0, k_end);
     };
     f32x16 acc[2][2];
 #pragma unroll
@@ -197,6 +216,7 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
 #pragma unroll
         for (int j = 0; j < 2; j++) acc[i][j] = f32x16{};
     const int r = lane & 31, kh = lane >> 5;
+    if (!BY_EXPERT) la.rows(P.a_gather, P.row2pair, P.top_k, m0, m_end, k_begin, k_end);
     if (k_begin < k_end) fetch(k_begin);
     for (int64_t k0 = k_begin; k0 < k_end; k0 += kBwdChunk) {
         __syncthreads();  // the previous chunk's fragments are read
