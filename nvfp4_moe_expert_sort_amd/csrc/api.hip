@@ -40,7 +40,7 @@ bool cfg_ok(const nvfp4moe_config* c) {
 
 struct Layout {
     nvfp4moe_ws_layout pub;
-    size_t blk_err, blk_counts, mtiles, n_mtiles, row_prob, xq_codes, xq_scales, gx;
+    size_t blk_err, blk_counts, mtiles, mtiles_even, n_mtiles, row_prob, xq_codes, xq_scales, gx;
     int64_t nblk_cap, mtiles_cap;
     size_t total;
 };
@@ -73,6 +73,7 @@ Layout make_layout(const nvfp4moe_config* c, int32_t capacity = 0) {
     L.pub.expert_off = take(4 * (E + 1));
     L.n_mtiles = take(4);
     L.mtiles = take(16 * L.mtiles_cap);
+    L.mtiles_even = take(16 * L.mtiles_cap);
     L.pub.pair2row = take(4 * std::max<int64_t>(P, 1));
     L.pub.row2pair = take(4 * rows);
     L.row_prob = take(4 * rows);
@@ -283,6 +284,7 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     rb.expert_count = (int32_t*)(ws + L.pub.expert_count);
     rb.expert_off = (int32_t*)(ws + L.pub.expert_off);
     rb.mtiles = (int4*)(ws + L.mtiles);
+    rb.mtiles_even = (int4*)(ws + L.mtiles_even);
     rb.n_mtiles = (int32_t*)(ws + L.n_mtiles);
     rb.err_word = (int32_t*)(ws + L.pub.err);
     rb.pair2row = (int32_t*)(ws + L.pub.pair2row);
@@ -357,7 +359,7 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     f1.K = (int32_t)H;
     f1.N = (int32_t)(2 * I);
     f1.n_tiles_n = col_tiles(I, kGemmSwiGLU);
-    f1.mtiles = rb.mtiles;
+    f1.mtiles = rb.mtiles_even;  // (the unfused plain GEMM below takes the 4-subtile table)
     f1.n_mtiles = rb.n_mtiles;
     f1.dense_m = -1;
     f1.out = (uint16_t*)(ws + L.pub.h);
@@ -371,6 +373,7 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
         // plain epilogue, whose arithmetic per element is the fused one's),
         // then h and its maxima from y1 in a separate kernel.
         GemmParams u = f1;
+        u.mtiles = rb.mtiles;
         u.N = (int32_t)(2 * I);
         u.n_tiles_n = col_tiles(2 * I, kGemmPlain);
         u.out = y1;

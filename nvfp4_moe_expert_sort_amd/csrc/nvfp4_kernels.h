@@ -41,7 +41,8 @@ struct RouteBuffers {
     int32_t* blk_err;      // [nblk]
     int32_t* expert_count; // [E]
     int32_t* expert_off;   // [E+1]
-    int4* mtiles;          // [mtiles_cap]
+    int4* mtiles;          // [mtiles_cap] 4-subtile row tiles, an expert's remainder last (FC2)
+    int4* mtiles_even;     // [mtiles_cap] the same tiles with each expert's subtiles spread evenly (FC1)
     int32_t* n_mtiles;     // [1]
     int32_t* err_word;     // [1]
     int32_t* pair2row;     // [T*K]

@@ -157,7 +157,8 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(int32_t nblk, int32_t 
                                                           const int32_t* __restrict__ blk_err,
                                                           int32_t* __restrict__ expert_count,
                                                           int32_t* __restrict__ expert_off,
-                                                          int4* __restrict__ mtiles, int32_t* __restrict__ n_mtiles,
+                                                          int4* __restrict__ mtiles, int4* __restrict__ mtiles_even,
+                                                          int32_t* __restrict__ n_mtiles,
                                                           int32_t* __restrict__ row2pair, int32_t* __restrict__ err_word) {
     __shared__ int32_t part[1024];
     __shared__ int2 wsum[16];
@@ -225,10 +226,21 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(int32_t nblk, int32_t 
             expert_off[E] = capacity > 0 ? E * capacity : incl.x;
             *n_mtiles = incl.y;
         }
+        // Two tables of the same row tiles: full 4-subtile tiles with the
+        // remainder last (9 subtiles: 4 + 4 + 1), and the expert's subtiles
+        // spread evenly (3 + 3 + 3).  A tile's weight streaming and decoding
+        // cost the same for any number of subtiles, so FC1 (K = H, long
+        // tiles) runs faster on the even split and FC2 (K = I) on the first.
+        const int32_t nsub_all = padded / kMAlign;
+        const int32_t base = ntile > 0 ? nsub_all / ntile : 0, extra = ntile > 0 ? nsub_all % ntile : 0;
+        int32_t r0e = off;
         for (int i = 0; i < ntile; i++) {
             const int32_t r0 = off + i * kTileRows;
             const int32_t nsub = min(kTileRows, padded - i * kTileRows) / kMAlign;
             mtiles[t0 + i] = make_int4(r0, tid, nsub, off + kept);
+            const int32_t nsub_e = base + (i < extra ? 1 : 0);
+            mtiles_even[t0 + i] = make_int4(r0e, tid, nsub_e, off + kept);
+            r0e += nsub_e * kMAlign;
         }
         for (int r = off + kept; r < off + padded; r++) row2pair[r] = -1;
     }
@@ -343,7 +355,8 @@ hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* prob
     hipError_t st = hipGetLastError();
     if (st != hipSuccess) return st;
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, nblk, E, capacity, rb.blk_counts, rb.blk_err,
-                       rb.expert_count, rb.expert_off, rb.mtiles, rb.n_mtiles, rb.row2pair, rb.err_word);
+                       rb.expert_count, rb.expert_off, rb.mtiles, rb.mtiles_even, rb.n_mtiles, rb.row2pair,
+                       rb.err_word);
     st = hipGetLastError();
     if (st != hipSuccess) return st;
     const int64_t P = (int64_t)T * K;
