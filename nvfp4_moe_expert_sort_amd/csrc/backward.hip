@@ -350,6 +350,11 @@ hipError_t launch_moe_backward(const BwdArgs& A, hipStream_t stream) {
     x1.ldc = H;
     e = launch_bwd_gemm(false, x1, A.mt_bound * x1.n_tiles_n, stream);
     if (e != hipSuccess) return e;
+    // dx = FP32 slot-order sum of each token's dxp rows (the forward's
+    // combine), while dxp is still in the last-level cache (the weight
+    // gradients' 2.4 GB of writes would evict it)
+    e = launch_combine(A.dxp, A.pair2row, A.T, (int32_t)H, A.top_k, A.dx, stream);
+    if (e != hipSuccess) return e;
     // dW2[e] = dout(rows of e)^T h(rows of e): A MC (dout rows, gathered), B MC (h rows)
     BwdGemmParams w2 = g;
     w2.a = A.dout;
@@ -385,9 +390,7 @@ hipError_t launch_moe_backward(const BwdArgs& A, hipStream_t stream) {
     w1.ldc = H;
     w1.c_estride = 2 * I * H;
     e = launch_bwd_gemm(true, w1, E * w1.n_tiles_m * w1.n_tiles_n, stream);
-    if (e != hipSuccess) return e;
-    // dx = FP32 slot-order sum of each token's dxp rows (the forward's combine)
-    return launch_combine(A.dxp, A.pair2row, A.T, (int32_t)H, A.top_k, A.dx, stream);
+    return e;
 }
 
 }  // namespace nvfp4
