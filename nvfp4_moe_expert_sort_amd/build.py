@@ -50,13 +50,16 @@ def _build_probe(item) -> str:
     return exe
 
 
-def build(jobs: int = 6) -> str:
+def build(jobs: int = 6, probes: bool = False) -> str:
+    """Compile every library source and link lib/libnvfp4moe.so; with
+    probes=True also the stand-alone measurement programs (not needed by the
+    library, its tests or bench.py)."""
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(os.path.dirname(LIB), exist_ok=True)
     with ThreadPoolExecutor(max(1, jobs)) as ex:
-        probes = ex.map(_build_probe, PROBES.items())
+        built = ex.map(_build_probe, PROBES.items()) if probes else iter(())
         objs = list(ex.map(_compile, SOURCES))
-        list(probes)
+        list(built)
     tmp = LIB + ".tmp"
     r = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
@@ -67,4 +70,5 @@ def build(jobs: int = 6) -> str:
 
 
 if __name__ == "__main__":
-    print(build())
+    import sys
+    print(build(probes="--probes" in sys.argv[1:]))
