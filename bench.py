@@ -240,7 +240,8 @@ def main():
             r_us = ev[0].elapsed_time(ev[1]) / 100 * 1e3
             r_bytes = n * H * 2 + E * H * 2 + n * E * 4 + n * K * 8
             router[f"T{n}"] = {"us": r_us, "tflops": 2.0 * n * H * E / (r_us / 1e6) / 1e12,
-                               "GB_s": r_bytes / (r_us / 1e6) / 1e9}
+                               "GB_s": r_bytes / (r_us / 1e6) / 1e9,
+                               "frac_hbm_peak": r_bytes / (r_us / 1e6) / 1e9 / HBM_PEAK_GBS}
         del w_r
 
     # Decode-sized forwards (secondary): the first n tokens of the workload, one
