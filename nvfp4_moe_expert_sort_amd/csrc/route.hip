@@ -20,6 +20,11 @@
 //   route_gather  per (32-row tile, up to 256 columns): builds the padded,
 //                 sorted GEMM-layout buffer from Xq, writing whole 1 KiB
 //                 chunks; padding rows are written as zeros.
+// Small batches (T*K <= 1024 pairs, T <= 128, E <= 256: decode sizes) take one launch,
+// route_small, for what route_count, route_scan and route_place do: one
+// workgroup ranks the pairs 64 at a time (one wavefront per group), adds the
+// groups' counts up per expert and places every pair, with the same ranks,
+// offsets, tables and error bits.
 // Integer atomics only on LDS counters: every count and row index is
 // independent of scheduling.
 //
@@ -248,6 +253,144 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(int32_t nblk, int32_t 
     if (tid == 0) *err_word = errs;
 }
 
+constexpr int kSmallPairs = 1024;  // pairs a single-workgroup sort takes (16 groups of 64)
+constexpr int kSmallExperts = 256;
+constexpr int kSmallTokens = 128;
+constexpr int kSmallWaves = 8;     // wavefront w takes the pair groups w and w + 8
+
+// The same per-row outputs as route_count + route_scan + route_place for
+// T*K <= kSmallPairs, T <= kSmallTokens and E <= kSmallExperts, in one
+// workgroup of 512 threads: group g of 64 pairs, [64 g, 64 g + 64), is ranked
+// by wavefront g % 8 (stable, pair order, by one ballot per id bit) and
+// counted per expert; thread e adds the 16 groups' counts up in group order
+// (a pair's rank = its group's prefix + its rank in the group: the same rank
+// as the block-wise path); the padded offsets and row-tile tables follow as
+// in route_scan.  Workgroups 1, 2, ... quantize the token rows, one per
+// wavefront (row 8 (b - 1) + w), once each.
+__global__ void __launch_bounds__(kSmallWaves * 64) route_small_kernel(const uint16_t* __restrict__ x,
+                                                           const int32_t* __restrict__ ids,
+                                                           const float* __restrict__ probs, int32_t T, int32_t H,
+                                                           int32_t K, int32_t E, int32_t capacity, int round_up,
+                                                           RouteBuffers rb) {
+    __shared__ int32_t gcnt[16][kSmallExperts];  // per group, then the group's exclusive prefix
+    __shared__ int32_t soff[kSmallExperts];
+    __shared__ int32_t pe[kSmallPairs], prank[kSmallPairs];  // each pair's expert and rank in its group
+    __shared__ int2 wsum[16];
+    __shared__ int32_t errs;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (blockIdx.x > 0) {
+        // Each wave quantizes its token row once (amax in the same pass).
+        const int64_t t = (int64_t)(blockIdx.x - 1) * kSmallWaves + wave;
+        if (t >= T) return;
+        const int64_t groups_per_lane = (H / 32 + kWave - 1) / kWave;
+        const bool ru = round_up != 0;
+        const uint16_t* xr = x + t * H;
+        switch (groups_per_lane) {
+            case 1: quant_row_regs<1>(xr, H, ru, false, t, rb.xq_codes, rb.xq_scales, rb.gx); break;
+            case 2: quant_row_regs<2>(xr, H, ru, false, t, rb.xq_codes, rb.xq_scales, rb.gx); break;
+            case 3: quant_row_regs<3>(xr, H, ru, false, t, rb.xq_codes, rb.xq_scales, rb.gx); break;
+            case 4: quant_row_regs<4>(xr, H, ru, false, t, rb.xq_codes, rb.xq_scales, rb.gx); break;
+            default: quant_row_wave(xr, H, -1.0f, ru, false, t, rb.xq_codes, rb.xq_scales, rb.gx); break;
+        }
+        return;
+    }
+    const int64_t P = (int64_t)T * K;
+    if (tid == 0) errs = 0;
+    if (tid < 16) wsum[tid] = make_int2(0, 0);
+    for (int i = tid; i < 16 * kSmallExperts; i += kSmallWaves * 64) (&gcnt[0][0])[i] = 0;
+    __syncthreads();
+    // (1) ranks within each group of 64 pairs, id checks
+    int err = 0;
+    int nbits = 0;
+    while ((1 << nbits) < E) nbits++;
+    for (int g = wave; g < 16; g += kSmallWaves) {
+        const int64_t p = (int64_t)g * kWave + lane;
+        const int32_t e = p < P ? ids[p] : -1;
+        const bool valid = e >= 0 && e < E;
+        if (p < P && !valid) err |= 1;
+        // A token may not name an expert twice: compare with its earlier slots,
+        // from the lanes that hold them (or memory across a group boundary).
+        const int kk = (int)((uint32_t)p % (uint32_t)K);
+        for (int d = 1; d < K; d++) {
+            const int32_t ed = __shfl(e, max(lane - d, 0), kWave);
+            if (valid && d <= kk) {
+                const int32_t prev = lane >= d ? ed : ids[p - d];
+                if (prev == e) err |= 2;
+            }
+        }
+        uint64_t mask = __ballot(valid);
+        for (int b = 0; b < nbits; b++) {
+            const bool bit = valid && ((e >> b) & 1);
+            const uint64_t m1 = __ballot(bit);
+            mask &= bit ? m1 : ~m1;
+        }
+        const uint64_t below = mask & ((1ull << lane) - 1ull);
+        pe[p] = valid ? e : -1;
+        prank[p] = (int32_t)__popcll(below);
+        if (valid && below == 0ull) gcnt[g][e] = (int32_t)__popcll(mask);
+    }
+    for (int o = 32; o > 0; o >>= 1) err |= __shfl_xor(err, o, kWave);
+    if (lane == 0 && err) atomicOr(&errs, err);
+    __syncthreads();
+    // (2) per expert: the groups' exclusive prefix, the total, the padded
+    //     offset and row tiles (as route_scan)
+    int32_t cnt = 0, kept = 0, padded = 0, ntile = 0;
+    if (tid < E) {
+        for (int g = 0; g < 16; g++) {
+            const int32_t c = gcnt[g][tid];
+            gcnt[g][tid] = cnt;
+            cnt += c;
+        }
+        kept = capacity > 0 ? min(cnt, capacity) : cnt;
+        padded = (kept + kMAlign - 1) / kMAlign * kMAlign;
+        ntile = (padded + kTileRows - 1) / kTileRows;
+        if (kept < cnt) atomicOr(&errs, 4);
+    }
+    const int2 incl = block_scan_incl2(make_int2(padded, ntile), wsum);
+    if (tid < E) {
+        const int32_t off = capacity > 0 ? tid * capacity : incl.x - padded;
+        const int32_t t0 = incl.y - ntile;
+        soff[tid] = off;
+        rb.expert_count[tid] = cnt;
+        rb.expert_off[tid] = off;
+        if (tid == E - 1) {
+            rb.expert_off[E] = capacity > 0 ? E * capacity : incl.x;
+            *rb.n_mtiles = incl.y;
+        }
+        const int32_t nsub_all = padded / kMAlign;
+        const int32_t base = ntile > 0 ? nsub_all / ntile : 0, extra = ntile > 0 ? nsub_all % ntile : 0;
+        int32_t r0e = off;
+        for (int i = 0; i < ntile; i++) {
+            const int32_t r0 = off + i * kTileRows;
+            const int32_t nsub = min(kTileRows, padded - i * kTileRows) / kMAlign;
+            rb.mtiles[t0 + i] = make_int4(r0, tid, nsub, off + kept);
+            const int32_t nsub_e = base + (i < extra ? 1 : 0);
+            rb.mtiles_even[t0 + i] = make_int4(r0e, tid, nsub_e, off + kept);
+            r0e += nsub_e * kMAlign;
+        }
+        for (int r = off + kept; r < off + padded; r++) rb.row2pair[r] = -1;
+    }
+    __syncthreads();
+    // (3) placement (as route_place)
+    for (int64_t p = tid; p < P; p += kSmallWaves * 64) {
+        const int32_t ep = pe[p];
+        if (ep < 0) {
+            rb.pair2row[p] = -1;
+        } else {
+            const int32_t local = gcnt[p / kWave][ep] + prank[p];
+            if (capacity > 0 && local >= capacity) {
+                rb.pair2row[p] = -1;
+            } else {
+                const int32_t row = soff[ep] + local;
+                rb.pair2row[p] = row;
+                rb.row2pair[row] = (int32_t)p;
+                rb.row_prob[row] = probs[p];
+            }
+        }
+    }
+    if (tid == 0) *rb.err_word = errs;
+}
+
 // pair2row[p] holds the pair's rank within (its block, its expert) on entry
 // and its sorted row on exit.
 __global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restrict__ ids,
@@ -347,23 +490,33 @@ __global__ void __launch_bounds__(256) route_gather_kernel(int32_t H, int32_t K,
 hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* probs, int32_t T, int32_t H, int32_t K,
                         int32_t E, int32_t capacity, bool round_up, const RouteBuffers& rb, int64_t rows_cap,
                         hipStream_t stream, bool quant_x) {
+    const int64_t P = (int64_t)T * K;
+    hipError_t st;
+    if (P <= kSmallPairs && T <= kSmallTokens && E <= kSmallExperts) {
+        // workgroup 0 sorts; with X to quantize, workgroups 1.. take 8 rows each
+        const unsigned qblocks = quant_x ? (unsigned)((T + kSmallWaves - 1) / kSmallWaves) : 0u;
+        hipLaunchKernelGGL(route_small_kernel, dim3(1 + qblocks), dim3(kSmallWaves * 64), 0, stream, x, ids, probs, T,
+                           H, K, E, capacity, round_up ? 1 : 0, rb);
+        st = hipGetLastError();
+        if (st != hipSuccess) return st;
+    } else {
     const int32_t nblk = (T + kTokPerBlk - 1) / kTokPerBlk;
     hipLaunchKernelGGL(route_count_kernel, dim3(nblk), dim3(kCountThreads), 0, stream, x, ids, T, H, K, E, round_up ? 1 : 0,
                        quant_x ? 1 : 0,
                        rb.blk_counts, rb.blk_err, rb.pair2row /* holds the ranks until route_place */, rb.xq_codes,
                        rb.xq_scales, rb.gx);
-    hipError_t st = hipGetLastError();
+    st = hipGetLastError();
     if (st != hipSuccess) return st;
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, nblk, E, capacity, rb.blk_counts, rb.blk_err,
                        rb.expert_count, rb.expert_off, rb.mtiles, rb.mtiles_even, rb.n_mtiles, rb.row2pair,
                        rb.err_word);
     st = hipGetLastError();
     if (st != hipSuccess) return st;
-    const int64_t P = (int64_t)T * K;
     hipLaunchKernelGGL(route_place_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, stream, ids, probs, P, K, E,
                        capacity, rb.blk_counts, rb.expert_off, rb.pair2row, rb.row2pair, rb.row_prob);
     st = hipGetLastError();
     if (st != hipSuccess) return st;
+    }
     if (!quant_x) return hipGetLastError();  // no quantized, sorted copy of X to build
     // Row tiles that can hold rows for this T (the device offsets decide
     // which are used): at most min(E, P) experts receive pairs, each padded

@@ -218,6 +218,19 @@ def test_qwen3_layer_all_tokens(gpu, orc, qwen3_layer):
     qwen3_layer.check(orc, wl.x, wl.ids, wl.probs, "qwen3 T=4096")
 
 
+def test_qwen3_sort_path_boundary(gpu, orc, qwen3_layer):
+    """The sort runs in one workgroup up to 1024 pairs and block-wise beyond:
+    the first 1, 8, 128 (1024 pairs) and 129 tokens of the layer, every stage
+    against the oracle, and each token's output bitwise the same on both sides
+    of the boundary."""
+    wl = qwen3_layer.wl
+    outs = {}
+    for T in (1, 8, 128, 129):
+        outs[T] = qwen3_layer.check(orc, wl.x[:T], wl.ids[:T], wl.probs[:T], f"qwen3 T={T}")
+    for T in (1, 8, 128):
+        assert np.array_equal(outs[T], outs[129][:T]), f"first {T} tokens"
+
+
 def test_skewed_layer_all_tokens(gpu, orc):
     """Zipf(1.1)-skewed routing, 16384 tokens (hottest expert ~15.9k rows, some
     with <= 8): every stage of every token element-wise against the oracle."""
