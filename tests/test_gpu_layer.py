@@ -231,6 +231,24 @@ def test_qwen3_sort_path_boundary(gpu, orc, qwen3_layer):
         assert np.array_equal(outs[T], outs[129][:T]), f"first {T} tokens"
 
 
+def test_device_error_word_blockwise_sort(gpu, qwen3_layer):
+    """The error word from the block-wise sort (more than 1024 pairs): an
+    out-of-range id sets bit 1, a repeated id bit 2, and a clean batch none."""
+    m = qwen3_layer.m
+    wl = qwen3_layer.wl
+    T = 200
+    ids = wl.ids[:T].copy()
+    ids[150, 3] = wl.shape.E
+    qwen3_layer.forward(wl.x[:T], ids, wl.probs[:T])
+    assert m.device_error(qwen3_layer.cfg, qwen3_layer.ws) & 1
+    ids = wl.ids[:T].copy()
+    ids[170, 5] = ids[170, 2]
+    qwen3_layer.forward(wl.x[:T], ids, wl.probs[:T])
+    assert m.device_error(qwen3_layer.cfg, qwen3_layer.ws) == 2
+    qwen3_layer.forward(wl.x[:T], wl.ids[:T], wl.probs[:T])
+    assert m.device_error(qwen3_layer.cfg, qwen3_layer.ws) == 0
+
+
 def test_skewed_layer_all_tokens(gpu, orc):
     """Zipf(1.1)-skewed routing, 16384 tokens (hottest expert ~15.9k rows, some
     with <= 8): every stage of every token element-wise against the oracle."""

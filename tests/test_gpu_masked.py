@@ -161,3 +161,34 @@ def test_masked_capacity_overflow(gpu, orc):
     # full experts hold exactly `capacity` rows, no padding
     assert np.all(mask.r2p[(np.arange(s.E) * capacity)[cont.cnt > capacity][:, None] + np.arange(capacity)] >= 0)
     print(f"  capacity {capacity}: {int(dropped.sum())} pairs dropped, {int(tok_ok.sum())} of {s.T} tokens unchanged")
+
+
+def test_masked_capacity_overflow_small_batch(gpu, orc):
+    """The same through the single-launch sort (800 pairs): the first 40 of 100
+    tokens all route to experts 0..7, which then hold 40 pairs each against a
+    capacity of 32."""
+    import types
+    m, dev = gpu
+    base = W.qwen3(seed=2, T=4096)
+    T, capacity, s_E = 100, 32, base.shape.E
+    ids = base.ids[:T].copy()
+    ids[:40] = np.arange(8, dtype=np.int32)[None, :]
+    for t in range(40, T):  # the other tokens keep away from experts 0..7
+        free = iter(e for e in range(8, s_E) if e not in ids[t])
+        ids[t] = [e if e >= 8 else next(free) for e in ids[t]]
+    s = W.MoEShape(T=T, H=base.shape.H, E=base.shape.E, K=base.shape.K, I=base.shape.I)
+    wl = types.SimpleNamespace(shape=s, x=base.x[:T], ids=ids, probs=base.probs[:T], weights=base.weights)
+    cont, mask = _both(m, dev, wl, capacity)
+    assert cont.err == 0 and mask.err == 4, f"error word {mask.err}"
+    check_route(orc, s.E, s.K, s.T, m.workspace_layout_masked(m.make_config(s.H, s.I, s.E, s.K, s.T), capacity),
+                mask.ws, ids, capacity)
+    e = ids.reshape(-1)
+    rank = cont.p2r - cont.off[e]
+    dropped = rank >= capacity
+    assert int(dropped.sum()) == 8 * 8
+    assert np.all(mask.p2r[dropped] == -1), "pairs past the capacity get no row"
+    _check_placement(cont, mask, np.nonzero(~dropped)[0], capacity, ids)
+    _check_experts(cont, mask, capacity)
+    tok_ok = ~dropped.reshape(s.T, s.K).any(axis=1)
+    assert tok_ok.sum() == T - 8
+    assert np.array_equal(mask.out[tok_ok], cont.out[tok_ok]), "tokens with no dropped pair keep their bits"
