@@ -20,11 +20,11 @@
 //   route_gather  per (32-row tile, up to 256 columns): builds the padded,
 //                 sorted GEMM-layout buffer from Xq, writing whole 1 KiB
 //                 chunks; padding rows are written as zeros.
-// Small batches (T*K <= 1024 pairs, T <= 128, E <= 256: decode sizes) take one launch,
-// route_small, for what route_count, route_scan and route_place do: one
-// workgroup ranks the pairs 64 at a time (one wavefront per group), adds the
-// groups' counts up per expert and places every pair, with the same ranks,
-// offsets, tables and error bits.
+// Small batches (T*K <= 1024 pairs, T <= 128, E <= 256: decode sizes) take
+// one launch, route_small, for what route_count, route_scan and route_place
+// do: its first workgroup ranks the pairs in groups of 64, adds the groups'
+// counts up per expert and places every pair, with the same ranks, offsets,
+// tables and error bits, while the other workgroups quantize X.
 // Integer atomics only on LDS counters: every count and row index is
 // independent of scheduling.
 //
