@@ -151,6 +151,11 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
         rg1 = NSUB > 2 ? P.a_g[row0 + min(64 + lane, kLastRow)] : 0.0f;
     }
 
+    // The weight global scales of this wave's columns (column l % 32 of each
+    // column tile), for the epilogue, loaded before the K loop.
+    float cg[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) cg[j] = P.b_g[(int64_t)expert * P.N + bcol0[j] - wcol + (lane & 31)];
     f32x16 acc[NSUB][2];
 #pragma unroll
     for (int i = 0; i < NSUB; i++) {
@@ -319,9 +324,6 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
     // the tile loop orders them against the next tile's LDS writes.  Nothing
     // here waits for the global stores.
     const int rowL = (lane >> 5) * 4;
-    float cg[2];
-#pragma unroll
-    for (int j = 0; j < 2; j++) cg[j] = P.b_g[(int64_t)expert * P.N + bcol0[j] + colL];
     float* RS = reinterpret_cast<float*>(&SB.b[wave][0][0][0]);
     if (MODE == kGemmPlain) {
         RS[lane] = rg0;
