@@ -22,9 +22,11 @@ runs continuously, whatever W is.
 from __future__ import annotations
 
 import argparse
+import glob
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -33,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense f16/bf16 MFMA
+NOMINAL_SCLK_MHZ = 2400.0       # the clock that peak assumes
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 MFMA (reported for context)
 HBM_PEAK_GBS = 8000.0
 
@@ -97,6 +100,59 @@ def fc1_traffic_bytes():
     if fields.get("kernel_source_sha256") != h.hexdigest() or "fc1_traffic_bytes_per_launch" not in fields:
         return None
     return float(fields["fc1_traffic_bytes_per_launch"])
+
+
+def sclk_path():
+    """The sysfs file listing the GPU's shader clock levels, the current one
+    marked with '*' (the first card that has one), or None."""
+    for p in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            open(p).read()
+            return p
+        except OSError:
+            continue
+    return None
+
+
+def read_sclk_mhz(path):
+    for line in open(path).read().splitlines():
+        if line.rstrip().endswith("*"):
+            tok = [t for t in line.replace(":", " ").split() if t.lower().endswith("mhz")]
+            if tok:
+                return float(tok[0][:-3])
+    return None
+
+
+def observed_clock(run, seconds=0.15, interval_s=0.002):
+    """Shader clock while `run()` keeps the GPU busy: pp_dpm_sclk read every
+    2 ms from a host thread over about `seconds` of back-to-back forwards (a
+    separate pass after the timed region, so the timing is not disturbed)."""
+    path = sclk_path()
+    if path is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            v = read_sclk_mhz(path)
+            if v is not None:
+                samples.append(v)
+            time.sleep(interval_s)
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        run()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    a = np.array(samples)
+    return {"source": path.replace("/sys/class/drm/", ""), "samples": int(a.size),
+            "median_mhz": float(np.median(a)), "p10_mhz": float(np.percentile(a, 10)),
+            "p90_mhz": float(np.percentile(a, 90)), "nominal_mhz": NOMINAL_SCLK_MHZ,
+            "what": "shader clock during back-to-back forwards of the headline workload"}
 
 
 def cpu_model() -> str:
@@ -441,6 +497,12 @@ def main():
     stage_ms = np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(m.N_STAGE_EVENTS - 1)] for ev in events])
     stage_mean = stage_ms.mean(axis=0)
 
+    def _fwd_batch():
+        for _ in range(10):
+            m.moe_expert_forward(cfg, x, ids, probs, qw, ws, out=out, stream=stream)
+        torch.cuda.synchronize()
+    clock = observed_clock(_fwd_batch)
+
     P = T * K
     layer_flop = 2.0 * P * 3 * H * I
     fc1_flop = 2.0 * P * H * 2 * I
@@ -471,7 +533,10 @@ def main():
                      "algorithmic_bytes": byts["fc1"],
                      "kernel": "gemm_kernel<SwiGLU> (FC1 grouped GEMM + router-weighted SwiGLU producer)",
                      "work_per_launch": f"2*T*K*H*2I = {fc1_flop:.4e} flop (useful rows only)",
-                     "avg_launch_ms": stage_mean[1]},
+                     "avg_launch_ms": stage_mean[1],
+                     "frac_at_observed_clock": (achieved / (MFMA_F16_PEAK_TFLOPS * clock["median_mhz"] / NOMINAL_SCLK_MHZ)
+                                                if clock else None)},
+        "clock": clock,
         "layer": {"tflops": layer_flop / layer_s / 1e12,
                   "frac_f16_mfma_peak": layer_flop / layer_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
                   "frac_fp4_mfma_peak": layer_flop / layer_s / 1e12 / MFMA_FP4_PEAK_TFLOPS,
