@@ -394,8 +394,12 @@ def main():
         torch.cuda.synchronize()
         sk_ms = ev[0].elapsed_time(ev[1]) / 30
         cnt = sk.expert_counts()
+        sk_tf = 2.0 * ss.T * K * 3 * H * I / (sk_ms / 1e3) / 1e12
+        sk_bytes = layer_bytes(ss.T, H, E, K, I, cnt)["total"]
         skewed = {"workload": sk.name, "tokens": ss.T, "ms_per_step": sk_ms, "tokens_per_s": ss.T / (sk_ms / 1e3),
-                  "tflops": 2.0 * ss.T * K * 3 * H * I / (sk_ms / 1e3) / 1e12,
+                  "tflops": sk_tf, "frac_f16_mfma_peak": sk_tf / MFMA_F16_PEAK_TFLOPS,
+                  "frac_fp4_mfma_peak": sk_tf / MFMA_FP4_PEAK_TFLOPS,
+                  "frac_hbm_peak": sk_bytes / (sk_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                   "expert_rows_min_max": [int(cnt.min()), int(cnt.max())]}
         del ws_s, xs_, ids_, pr_, out_
 
