@@ -2,9 +2,10 @@
 // checks (before any launch), workspace carving, launch order, self-test.
 //
 // The forward enqueues, on the caller's stream and with no host sync:
-//   route_hist -> route_scan -> route_scatter (sort + amax + quantize X into
-//   the padded GEMM-layout buffer) -> FC1 grouped GEMM with the router-weighted
-//   SwiGLU producer (h and its per-tile maxima) -> quantize h -> FC2 grouped
+//   route_count -> route_scan -> route_place (route_small alone up to 1024
+//   pairs) -> route_gather (sort + amax + quantize X into the padded
+//   GEMM-layout buffer) -> FC1 grouped GEMM with the router-weighted SwiGLU
+//   producer (h and its per-32-column maxima) -> quantize h -> FC2 grouped
 //   GEMM -> slot-order combine.
 // (miniTE summary page, "how to use it"; article sections 4.4-4.6.)
 #include <hip/hip_runtime.h>

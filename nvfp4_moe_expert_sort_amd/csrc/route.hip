@@ -4,8 +4,9 @@
 // boundaries are device offsets; the metadata is reused by FC1, FC2 and the
 // combine).
 //
-// Four launches, all sized from T and the config only (no host read-back of
-// counts, article section 4.6):
+// Four launches (two up to 1024 pairs, see route_small below), all sized
+// from T and the config only (no host read-back of counts, article section
+// 4.6):
 //   route_count   per block of 16 tokens, one wavefront per token: the row
 //                 is read once into registers for its amax and quantization
 //                 (token-major buffer Xq; skipped for BF16 activations, the
