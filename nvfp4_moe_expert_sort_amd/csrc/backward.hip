@@ -251,7 +251,10 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
                     if (row < row_end && row < m_end)
                         reinterpret_cast<uint16_t*>(P.out)[row * P.ldc + col] = (uint16_t)bf16_hw(acc[i][j][q]);
                 } else if (row < m_end) {
-                    reinterpret_cast<float*>(P.out)[expert * P.c_estride + row * P.ldc + col] = acc[i][j][q];
+                    // the weight gradients (2.4 GB at the Qwen3 shape) are
+                    // written once and not read here: non-temporal stores
+                    __builtin_nontemporal_store(acc[i][j][q],
+                                                &reinterpret_cast<float*>(P.out)[expert * P.c_estride + row * P.ldc + col]);
                 }
             }
 }
