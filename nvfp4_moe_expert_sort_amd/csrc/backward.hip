@@ -16,9 +16,11 @@
 // with gate, up the forward's BF16 FC1 output y1 and h its BF16 FC2 input.
 //
 // One GEMM kernel serves the four products: a workgroup of 4 wavefronts owns
-// a 128 x 128 output tile (each wave 64 x 64 = 2 x 2 MFMA tiles of
-// v_mfma_f32_32x32x16_bf16, FP32 accumulation) and walks K in chunks of 64
-// through LDS, each operand staged as memory gives it (16-byte stores).  An
+// an output tile -- 128 x 256 for dh and dxp (each wave all 128 rows x 64
+// columns, 4 x 2 MFMA tiles, so each A fragment feeds two MFMAs and each B
+// fragment four), 128 x 128 for the weight gradients (each wave 64 x 64) --
+// of v_mfma_f32_32x32x16_bf16 with FP32 accumulation, and walks K in chunks
+// of 64 through LDS, each operand staged as memory gives it (16-byte stores).  An
 // operand whose memory rows run along k (the activations of dh and dxp) gives
 // each MFMA fragment in one 16-byte LDS read; one whose rows run along the
 // output index (the weights; both operands of the weight gradients, whose k
@@ -38,9 +40,8 @@ constexpr int kBwdThreads = 256;
 constexpr int kBwdTile = 128;   // output rows and columns per workgroup
 constexpr int kBwdChunk = 64;   // k per LDS chunk (four MFMA k-steps)
 constexpr int kKcPitch = kBwdChunk + 8;  // halves per LDS row of a KC operand, [index][k]
-constexpr int kMcPitch = kBwdTile + 8;   // halves per LDS row of an MC operand, [k][index]
-constexpr int kBwdPieces = kBwdTile * kBwdChunk / 8 / kBwdThreads;  // 16-byte pieces per thread and operand
-constexpr int kBwdOperandLds = (kBwdTile * kKcPitch > kBwdChunk * kMcPitch ? kBwdTile * kKcPitch : kBwdChunk * kMcPitch);
+constexpr int kBwdOperandLds = kBwdTile * kKcPitch;  // a KC operand, or an MC operand 128 wide
+constexpr int kBwdOperandLdsWide = kBwdChunk * (2 * kBwdTile + 8);  // an MC operand 256 wide
 
 // Row of an operand in memory: identity, or the token of a sorted row (through
 // row2pair; padding rows, -1, read token 0 and are never stored or are zero-filled).
@@ -55,8 +56,10 @@ __device__ __forceinline__ int64_t bwd_row(int64_t r, bool gather, const int32_t
 // an MFMA fragment (8 consecutive k of one index) is one 16-byte read.  MC
 // (memory rows run along the index): LDS [k][index], and a fragment is two
 // transposing 8-byte reads.
-template <bool KC>
+template <bool KC, int W = kBwdTile>
 struct BwdLoad {
+    static constexpr int kMcPitch = W + 8;  // halves per LDS row of an MC operand, [k][index]
+    static constexpr int kBwdPieces = W * kBwdChunk / 8 / kBwdThreads;  // 16-byte pieces per thread
     u32x4 v[kBwdPieces];
     bool live[kBwdPieces];
     // Memory rows of this thread's pieces: KC, the tile's index rows (the same
@@ -70,8 +73,8 @@ struct BwdLoad {
             if (KC) {  // 128 index rows x 8 pieces of 8 k
                 const int64_t i = idx0 + piece / (kBwdChunk / 8);
                 mrow[h] = (int32_t)bwd_row(i < idx_end ? i : idx0, gather, row2pair, K);
-            } else {  // 64 k rows x 16 pieces of 8 indices
-                const int64_t k = k0 + piece / (kBwdTile / 8);
+            } else {  // 64 k rows x W / 8 pieces of 8 indices
+                const int64_t k = k0 + piece / (W / 8);
                 // rows past the end (or of an empty range) look up an in-bounds row; never used
                 const int64_t kk = k < k_end ? k : k_end - 1;
                 mrow[h] = (int32_t)bwd_row(kk > 0 ? kk : 0, gather, row2pair, K);
@@ -88,8 +91,9 @@ struct BwdLoad {
                 live[h] = idx0 + piece / (kBwdChunk / 8) < idx_end;
                 col = k0 + 8 * (piece % (kBwdChunk / 8));
             } else {
-                live[h] = k0 + piece / (kBwdTile / 8) < k_end;
-                col = idx0 + 8 * (piece % (kBwdTile / 8));
+                live[h] = k0 + piece / (W / 8) < k_end;
+                col = idx0 + 8 * (piece % (W / 8));
+                col = col < idx_end ? col : idx_end - 8;  // columns past the end (a partial tile) re-read the last 8
             }
             v[h] = *reinterpret_cast<const u32x4*>(base + (int64_t)mrow[h] * ld + col);
         }
@@ -100,7 +104,7 @@ struct BwdLoad {
             const int piece = threadIdx.x + h * kBwdThreads;
             const u32x4 w = live[h] ? v[h] : u32x4{0u, 0u, 0u, 0u};
             const int at = KC ? (piece / (kBwdChunk / 8)) * kKcPitch + 8 * (piece % (kBwdChunk / 8))
-                              : (piece / (kBwdTile / 8)) * kMcPitch + 8 * (piece % (kBwdTile / 8));
+                              : (piece / (W / 8)) * kMcPitch + 8 * (piece % (W / 8));
             *reinterpret_cast<u32x4*>(lds + at) = w;
         }
     }
@@ -160,10 +164,14 @@ struct BwdGemmParams {
 // MC, FP32 output).
 template <bool BY_EXPERT>
 __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams P) {
+    // (row-tile cases: 128 x 256 tiles, each wave all 128 rows x 64 columns;
+    // weight gradients: 128 x 128 tiles, waves 2 x 2 of 64 x 64)
+    constexpr int TN = BY_EXPERT ? kBwdTile : 2 * kBwdTile;
+    constexpr int NI = BY_EXPERT ? 2 : 4;  // 32-row MFMA tiles per wave
     __shared__ __attribute__((aligned(16))) uint16_t SA[kBwdOperandLds];
-    __shared__ __attribute__((aligned(16))) uint16_t SB[kBwdOperandLds];
+    __shared__ __attribute__((aligned(16))) uint16_t SB[BY_EXPERT ? kBwdOperandLds : kBwdOperandLdsWide];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = BY_EXPERT ? (wave & 1) : 0, wn = BY_EXPERT ? (wave >> 1) : wave;
     // Workgroup b runs on XCD b % 8 (round-robin dispatch), and XCD x takes
     // the contiguous range [x * span, (x + 1) * span) of the tile list, in
     // which tiles that share an expert's operands (its weights, or its rows of
@@ -183,7 +191,7 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
         m_end = d.x + 32 * d.z;
         row_end = d.w;
         expert = d.y;
-        n0 = (tile % P.n_tiles_n) * kBwdTile;
+        n0 = (tile % P.n_tiles_n) * TN;
         k_begin = 0;
         k_end = P.Kd;
     } else {
@@ -198,7 +206,7 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
     }
     const uint16_t* bbase = P.b + expert * P.b_estride;
     BwdLoad<!BY_EXPERT> la;
-    BwdLoad<false> lb;
+    BwdLoad<false, TN> lb;
     // A: BY_EXPERT false, KC with memory rows m (sorted rows); true, MC with
     // memory rows k (sorted rows).  B: MC with memory rows k -- an expert's
     // weight rows, or sorted rows.
@@ -210,9 +218,9 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
         la.fetch(P.a, P.lda, m0, m_end, k0, k_end);
         lb.fetch(bbase, P.ldb, n0, P.N, k0, k_end);
     };
-    f32x16 acc[2][2];
+    f32x16 acc[NI][2];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < NI; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++) acc[i][j] = f32x16{};
     const int r = lane & 31, kh = lane >> 5;
@@ -226,13 +234,13 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
         if (k0 + kBwdChunk < k_end) fetch(k0 + kBwdChunk);  // next chunk in flight during the MFMAs
 #pragma unroll
         for (int ks = 0; ks < kBwdChunk / 16; ks++) {
-            bf16x8b af[2], bfr[2];
+            bf16x8b af[NI], bfr[2];
 #pragma unroll
-            for (int i = 0; i < 2; i++) af[i] = la.frag(SA, 64 * wm + 32 * i, 16 * ks);
+            for (int i = 0; i < NI; i++) af[i] = la.frag(SA, 64 * wm + 32 * i, 16 * ks);
 #pragma unroll
             for (int j = 0; j < 2; j++) bfr[j] = lb.frag(SB, 64 * wn + 32 * j, 16 * ks);
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int i = 0; i < NI; i++)
 #pragma unroll
                 for (int j = 0; j < 2; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
@@ -240,13 +248,14 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
     }
     // register q of tile (i, j): row 64 wm + 32 i + (q/4)*8 + kh*4 + q%4, column 64 wn + 32 j + r
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < NI; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int q = 0; q < 16; q++) {
                 const int64_t row = m0 + 64 * wm + 32 * i + (q >> 2) * 8 + kh * 4 + (q & 3);
                 const int64_t col = n0 + 64 * wn + 32 * j + r;
+                if (col >= P.N) continue;  // a partial column tile
                 if (!BY_EXPERT) {
                     if (row < row_end && row < m_end)
                         reinterpret_cast<uint16_t*>(P.out)[row * P.ldc + col] = (uint16_t)bf16_hw(acc[i][j][q]);
@@ -327,7 +336,7 @@ hipError_t launch_moe_backward(const BwdArgs& A, hipStream_t stream) {
     g.b_gather = false;
     g.N = (int32_t)I;
     g.Kd = (int32_t)H;
-    g.n_tiles_n = (int32_t)(I / kBwdTile);
+    g.n_tiles_n = (int32_t)((I + 2 * kBwdTile - 1) / (2 * kBwdTile));
     g.out = A.dh;
     g.ldc = I;
     hipError_t e = launch_bwd_gemm(false, g, A.mt_bound * g.n_tiles_n, stream);
@@ -348,7 +357,7 @@ hipError_t launch_moe_backward(const BwdArgs& A, hipStream_t stream) {
     x1.b_estride = 2 * I * H;
     x1.N = (int32_t)H;
     x1.Kd = (int32_t)(2 * I);
-    x1.n_tiles_n = (int32_t)(H / kBwdTile);
+    x1.n_tiles_n = (int32_t)((H + 2 * kBwdTile - 1) / (2 * kBwdTile));
     x1.out = A.dxp;
     x1.ldc = H;
     e = launch_bwd_gemm(false, x1, A.mt_bound * x1.n_tiles_n, stream);
