@@ -35,13 +35,22 @@
 namespace nvfp4 {
 
 typedef __bf16 bf16x8b __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBwdThreads = 256;
 constexpr int kBwdTile = 128;   // output rows and columns per workgroup
 constexpr int kBwdChunk = 64;   // k per LDS chunk (four MFMA k-steps)
 constexpr int kKcPitch = kBwdChunk + 8;  // halves per LDS row of a KC operand, [index][k]
-constexpr int kBwdOperandLds = kBwdTile * kKcPitch;  // a KC operand, or an MC operand 128 wide
-constexpr int kBwdOperandLdsWide = kBwdChunk * (2 * kBwdTile + 8);  // an MC operand 256 wide
+// An MC operand's LDS rows are padded by 32 halves: the 32 lanes of one
+// transposing fragment read cover four rows of 64 bytes, which a row pitch of
+// 64 mod 256 bytes puts on disjoint banks (with 8 halves of padding they
+// overlap 2-4 ways).
+constexpr int kMcPad = 32;
+constexpr int kBwdOperandLds = kBwdTile * kKcPitch > kBwdChunk * (kBwdTile + kMcPad)
+                                   ? kBwdTile * kKcPitch
+                                   : kBwdChunk * (kBwdTile + kMcPad);  // a KC operand, or an MC operand 128 wide
+constexpr int kBwdOperandLdsWide = kBwdChunk * (2 * kBwdTile + kMcPad);  // an MC operand 256 wide
+constexpr int kBwdWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0)
 
 // Row of an operand in memory: identity, or the token of a sorted row (through
 // row2pair; padding rows, -1, read token 0 and are never stored or are zero-filled).
@@ -58,7 +67,7 @@ __device__ __forceinline__ int64_t bwd_row(int64_t r, bool gather, const int32_t
 // transposing 8-byte reads.
 template <bool KC, int W = kBwdTile>
 struct BwdLoad {
-    static constexpr int kMcPitch = W + 8;  // halves per LDS row of an MC operand, [k][index]
+    static constexpr int kMcPitch = W + kMcPad;  // halves per LDS row of an MC operand, [k][index]
     static constexpr int kBwdPieces = W * kBwdChunk / 8 / kBwdThreads;  // 16-byte pieces per thread
     u32x4 v[kBwdPieces];
     bool live[kBwdPieces];
@@ -67,6 +76,19 @@ struct BwdLoad {
     int32_t mrow[kBwdPieces];  // memory row indices are < 2^31
     __device__ __forceinline__ void rows(bool gather, const int32_t* row2pair, int32_t K, int64_t idx0,
                                          int64_t idx_end, int64_t k0, int64_t k_end) {
+        if (!KC && gather && W == kBwdTile) {
+            // A gathered MC chunk: piece h of thread (wave w, lane l) is k row
+            // k0 + 4 w + l / 16 + 16 h, so a wave touches 16 rows.  Lane
+            // a + 4 h (a < 4) looks row k0 + 4 w + a + 16 h up once and the
+            // threads take it from there.
+            const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+            const int64_t k = k0 + 4 * wave + (lane & 3) + 16 * ((lane >> 2) & 3);
+            const int64_t kk = k < k_end ? k : k_end - 1;
+            const int32_t r = (int32_t)bwd_row(kk > 0 ? kk : 0, true, row2pair, K);
+#pragma unroll
+            for (int h = 0; h < kBwdPieces; h++) mrow[h] = __shfl(r, (lane >> 4) + 4 * h, kWave);
+            return;
+        }
 #pragma unroll
         for (int h = 0; h < kBwdPieces; h++) {
             const int piece = threadIdx.x + h * kBwdThreads;
@@ -168,8 +190,11 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
     // weight gradients: 128 x 128 tiles, waves 2 x 2 of 64 x 64)
     constexpr int TN = BY_EXPERT ? kBwdTile : 2 * kBwdTile;
     constexpr int NI = BY_EXPERT ? 2 : 4;  // 32-row MFMA tiles per wave
-    __shared__ __attribute__((aligned(16))) uint16_t SA[kBwdOperandLds];
-    __shared__ __attribute__((aligned(16))) uint16_t SB[BY_EXPERT ? kBwdOperandLds : kBwdOperandLdsWide];
+    // the two operand buffers, and after the K loop the output staging
+    constexpr int kSA = kBwdOperandLds, kSB = BY_EXPERT ? kBwdOperandLds : kBwdOperandLdsWide;
+    __shared__ __attribute__((aligned(16))) uint16_t LDS[kSA + kSB];
+    uint16_t* const SA = LDS;
+    uint16_t* const SB = LDS + kSA;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = BY_EXPERT ? (wave & 1) : 0, wn = BY_EXPERT ? (wave >> 1) : wave;
     // Workgroup b runs on XCD b % 8 (round-robin dispatch), and XCD x takes
@@ -246,26 +271,66 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
     }
-    // register q of tile (i, j): row 64 wm + 32 i + (q/4)*8 + kh*4 + q%4, column 64 wn + 32 j + r
+    // Epilogue.  Register q of MFMA tile (i, j) holds row 64 wm + 32 i +
+    // (q/4)*8 + kh*4 + q%4 and column 64 wn + 32 j + r of the wave's part of
+    // the tile.  The values pass through the wave's own slice of the operand
+    // buffers, one 32-row MFMA tile at a time, so that every global store is
+    // 16 bytes per lane over whole rows of 128 (BF16) or 256 (FP32) bytes:
+    // a quarter to an eighth of the store instructions of per-element stores,
+    // which compete with the operand loads for the CU's address unit.
+    __syncthreads();  // every wave's last fragment reads are done
+    if (!BY_EXPERT) {
+        constexpr int kP = 64;  // halves per staged row
+        uint16_t* const E = LDS + wave * (32 * kP);
 #pragma unroll
-    for (int i = 0; i < NI; i++)
+        for (int i = 0; i < NI; i++) {
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+            for (int j = 0; j < 2; j++)
 #pragma unroll
-            for (int q = 0; q < 16; q++) {
-                const int64_t row = m0 + 64 * wm + 32 * i + (q >> 2) * 8 + kh * 4 + (q & 3);
-                const int64_t col = n0 + 64 * wn + 32 * j + r;
-                if (col >= P.N) continue;  // a partial column tile
-                if (!BY_EXPERT) {
-                    if (row < row_end && row < m_end)
-                        reinterpret_cast<uint16_t*>(P.out)[row * P.ldc + col] = (uint16_t)bf16_hw(acc[i][j][q]);
-                } else if (row < m_end) {
-                    // the weight gradients (2.4 GB at the Qwen3 shape) are
-                    // written once and not read here: non-temporal stores
-                    __builtin_nontemporal_store(acc[i][j][q],
-                                                &reinterpret_cast<float*>(P.out)[expert * P.c_estride + row * P.ldc + col]);
-                }
+                for (int q = 0; q < 16; q++)
+                    E[((q >> 2) * 8 + kh * 4 + (q & 3)) * kP + 32 * j + r] = (uint16_t)bf16_hw(acc[i][j][q]);
+            __builtin_amdgcn_s_waitcnt(kBwdWaitLgkm0);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int u = 0; u < 4; u++) {  // 8 lanes per row of 64 columns
+                const int rl = 8 * u + (lane >> 3), cl = 8 * (lane & 7);
+                const u32x4 v = *reinterpret_cast<const u32x4*>(E + rl * kP + cl);
+                const int64_t row = m0 + 32 * i + rl;
+                const int64_t col = n0 + 64 * wn + cl;
+                if (row < row_end && row < m_end && col < P.N)  // rows past the expert's end, a partial column tile
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(P.out) + row * P.ldc + col) = v;
             }
+            __builtin_amdgcn_s_waitcnt(kBwdWaitLgkm0);  // the slice is read before the next tile overwrites it
+            __builtin_amdgcn_wave_barrier();
+        }
+    } else {
+        constexpr int kP = 72;  // floats per staged row: rows 4 apart on disjoint banks
+        float* const E = reinterpret_cast<float*>(LDS) + wave * (32 * kP);
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int q = 0; q < 16; q++) E[((q >> 2) * 8 + kh * 4 + (q & 3)) * kP + 32 * j + r] = acc[i][j][q];
+            __builtin_amdgcn_s_waitcnt(kBwdWaitLgkm0);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int u = 0; u < 8; u++) {  // 16 lanes per row of 64 columns
+                const int rl = 4 * u + (lane >> 4), cl = 4 * (lane & 15);
+                const f32x4 v = *reinterpret_cast<const f32x4*>(E + rl * kP + cl);
+                const int64_t row = m0 + 64 * wm + 32 * i + rl;
+                const int64_t col = n0 + 64 * wn + cl;
+                // the weight gradients (2.4 GB at the Qwen3 shape) are written
+                // once and not read here: non-temporal stores
+                if (row < m_end && col < P.N)
+                    __builtin_nontemporal_store(
+                        v, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(P.out) + expert * P.c_estride +
+                                                    row * P.ldc + col));
+            }
+            __builtin_amdgcn_s_waitcnt(kBwdWaitLgkm0);
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
 }
 
 // SwiGLU backward per sorted row holding a pair (one wavefront per row):
