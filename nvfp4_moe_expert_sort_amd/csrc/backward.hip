@@ -52,82 +52,103 @@ constexpr int kBwdOperandLds = kBwdTile * kKcPitch > kBwdChunk * (kBwdTile + kMc
 constexpr int kBwdOperandLdsWide = kBwdChunk * (2 * kBwdTile + kMcPad);  // an MC operand 256 wide
 constexpr int kBwdWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0)
 
-// Row of an operand in memory: identity, or the token of a sorted row (through
-// row2pair; padding rows, -1, read token 0 and are never stored or are zero-filled).
-__device__ __forceinline__ int64_t bwd_row(int64_t r, bool gather, const int32_t* row2pair, int32_t K) {
-    if (!gather) return r;
-    const int32_t p = row2pair[r];
-    return p >= 0 ? (int64_t)((uint32_t)p / (uint32_t)K) : 0;
+// Token of a sorted row from its row2pair entry (padding rows, -1, read token
+// 0 and are never stored or are zero-filled).
+__device__ __forceinline__ int32_t bwd_token(int32_t p, int32_t K) {
+    return p >= 0 ? (int32_t)((uint32_t)p / (uint32_t)K) : 0;
 }
 
-// One 64-deep chunk of a 128-wide operand tile, staged in LDS as memory gives
+// One 64-deep chunk of an operand tile W wide, staged in LDS as memory gives
 // it, 16 bytes per store.  KC (memory rows run along k): LDS [index][k], and
 // an MFMA fragment (8 consecutive k of one index) is one 16-byte read.  MC
 // (memory rows run along the index): LDS [k][index], and a fragment is two
-// transposing 8-byte reads.
+// transposing 8-byte reads.  Row and column indices are 32-bit (sorted rows
+// < 2^30); a piece's offset is one 32 x 32 -> 64-bit multiply-add.
 template <bool KC, int W = kBwdTile>
 struct BwdLoad {
     static constexpr int kMcPitch = W + kMcPad;  // halves per LDS row of an MC operand, [k][index]
     static constexpr int kBwdPieces = W * kBwdChunk / 8 / kBwdThreads;  // 16-byte pieces per thread
+    static constexpr int kRowsPerWave = 512 / W;  // MC: k rows a wave's pieces share per h
     u32x4 v[kBwdPieces];
-    bool live[kBwdPieces];
     // Memory rows of this thread's pieces: KC, the tile's index rows (the same
     // for every chunk, looked up once per tile); MC, the k rows of a chunk.
-    int32_t mrow[kBwdPieces];  // memory row indices are < 2^31
-    __device__ __forceinline__ void rows(bool gather, const int32_t* row2pair, int32_t K, int64_t idx0,
-                                         int64_t idx_end, int64_t k0, int64_t k_end) {
-        if (!KC && gather && W == kBwdTile) {
-            // A gathered MC chunk: piece h of thread (wave w, lane l) is k row
-            // k0 + 4 w + l / 16 + 16 h, so a wave touches 16 rows.  Lane
-            // a + 4 h (a < 4) looks row k0 + 4 w + a + 16 h up once and the
-            // threads take it from there.
-            const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-            const int64_t k = k0 + 4 * wave + (lane & 3) + 16 * ((lane >> 2) & 3);
-            const int64_t kk = k < k_end ? k : k_end - 1;
-            const int32_t r = (int32_t)bwd_row(kk > 0 ? kk : 0, true, row2pair, K);
-#pragma unroll
-            for (int h = 0; h < kBwdPieces; h++) mrow[h] = __shfl(r, (lane >> 4) + 4 * h, kWave);
-            return;
-        }
+    int32_t mrow[kBwdPieces];
+    int32_t praw;  // a gathered MC operand: row2pair entry of this lane's row of the next chunk
+    // KC: the tile's rows, once per tile (gathered ones looked up per piece).
+    __device__ __forceinline__ void kc_rows(bool gather, const int32_t* row2pair, int32_t K, int32_t idx0,
+                                            int32_t idx_end) {
 #pragma unroll
         for (int h = 0; h < kBwdPieces; h++) {
             const int piece = threadIdx.x + h * kBwdThreads;
-            if (KC) {  // 128 index rows x 8 pieces of 8 k
-                const int64_t i = idx0 + piece / (kBwdChunk / 8);
-                mrow[h] = (int32_t)bwd_row(i < idx_end ? i : idx0, gather, row2pair, K);
-            } else {  // 64 k rows x W / 8 pieces of 8 indices
-                const int64_t k = k0 + piece / (W / 8);
-                // rows past the end (or of an empty range) look up an in-bounds row; never used
-                const int64_t kk = k < k_end ? k : k_end - 1;
-                mrow[h] = (int32_t)bwd_row(kk > 0 ? kk : 0, gather, row2pair, K);
-            }
+            const int32_t i = idx0 + piece / (kBwdChunk / 8);  // 128 index rows x 8 pieces of 8 k
+            const int32_t ii = i < idx_end ? i : idx0;
+            mrow[h] = gather ? bwd_token(row2pair[ii], K) : ii;
         }
     }
-    __device__ __forceinline__ void fetch(const uint16_t* base, int64_t ld, int64_t idx0, int64_t idx_end, int64_t k0,
-                                          int64_t k_end) {
+    // MC: piece h of thread (wave w, lane l) is k row
+    // k0 + R w + l / (W / 8) + (2048 / W) h with R = 512 / W, so a wave
+    // touches 16 rows.  Rows past the end (or of an empty range) take an
+    // in-bounds row; never used.
+    __device__ __forceinline__ void mc_rows(int32_t k0, int32_t k_end) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int h = 0; h < kBwdPieces; h++) {
+            const int32_t k = k0 + kRowsPerWave * wave + lane / (W / 8) + (2048 / W) * h;
+            const int32_t kk = k < k_end ? k : k_end - 1;
+            mrow[h] = kk > 0 ? kk : 0;
+        }
+    }
+    // A gathered MC operand: lane s < 16 (and its copies s + 16 j) looks up
+    // row k0 + R w + s % R + (2048 / W) (s / R) of chunk k0 a chunk ahead of
+    // its use ...
+    __device__ __forceinline__ void mc_prefetch(const int32_t* row2pair, int32_t k0, int32_t k_end) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, s = lane & 15;
+        const int32_t k = k0 + kRowsPerWave * wave + s % kRowsPerWave + (2048 / W) * (s / kRowsPerWave);
+        const int32_t kk = k < k_end ? k : k_end - 1;
+        praw = row2pair[kk > 0 ? kk : 0];
+    }
+    // ... and piece h of lane l takes the token from lane l / (W / 8) + R h.
+    __device__ __forceinline__ void mc_gathered_rows(int32_t K) {
+        const int lane = threadIdx.x & 63;
+        const int32_t t = bwd_token(praw, K);
+#pragma unroll
+        for (int h = 0; h < kBwdPieces; h++) mrow[h] = __shfl(t, lane / (W / 8) + kRowsPerWave * h, kWave);
+    }
+    __device__ __forceinline__ void fetch(const uint16_t* base, int64_t ld, int32_t idx0, int32_t idx_end,
+                                          int32_t k0) {
 #pragma unroll
         for (int h = 0; h < kBwdPieces; h++) {
             const int piece = threadIdx.x + h * kBwdThreads;
-            int64_t col;
+            int32_t col;
             if (KC) {
-                live[h] = idx0 + piece / (kBwdChunk / 8) < idx_end;
                 col = k0 + 8 * (piece % (kBwdChunk / 8));
             } else {
-                live[h] = k0 + piece / (W / 8) < k_end;
                 col = idx0 + 8 * (piece % (W / 8));
                 col = col < idx_end ? col : idx_end - 8;  // columns past the end (a partial tile) re-read the last 8
             }
-            v[h] = *reinterpret_cast<const u32x4*>(base + (int64_t)mrow[h] * ld + col);
+            const uint64_t off = (uint64_t)(uint32_t)mrow[h] * (uint32_t)ld + (uint32_t)col;
+            v[h] = *reinterpret_cast<const u32x4*>(base + off);
         }
     }
-    __device__ __forceinline__ void store(uint16_t* lds) const {
+    // Pieces of rows past the end are stored as zeros (mask: the chunk or tile
+    // has such rows; a uniform test, so full chunks skip the selects).
+    __device__ __forceinline__ static int lds_at(int piece) {
+        return KC ? (piece / (kBwdChunk / 8)) * kKcPitch + 8 * (piece % (kBwdChunk / 8))
+                  : (piece / (W / 8)) * kMcPitch + 8 * (piece % (W / 8));
+    }
+    __device__ __forceinline__ void store(uint16_t* lds, bool mask, int32_t idx0, int32_t idx_end, int32_t k0,
+                                          int32_t k_end) const {
+        if (__builtin_expect(mask, 0)) {
 #pragma unroll
-        for (int h = 0; h < kBwdPieces; h++) {
-            const int piece = threadIdx.x + h * kBwdThreads;
-            const u32x4 w = live[h] ? v[h] : u32x4{0u, 0u, 0u, 0u};
-            const int at = KC ? (piece / (kBwdChunk / 8)) * kKcPitch + 8 * (piece % (kBwdChunk / 8))
-                              : (piece / (W / 8)) * kMcPitch + 8 * (piece % (W / 8));
-            *reinterpret_cast<u32x4*>(lds + at) = w;
+            for (int h = 0; h < kBwdPieces; h++) {
+                const int piece = threadIdx.x + h * kBwdThreads;
+                const bool live = KC ? idx0 + piece / (kBwdChunk / 8) < idx_end : k0 + piece / (W / 8) < k_end;
+                *reinterpret_cast<u32x4*>(lds + lds_at(piece)) = live ? v[h] : u32x4{0u, 0u, 0u, 0u};
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < kBwdPieces; h++)
+                *reinterpret_cast<u32x4*>(lds + lds_at(threadIdx.x + h * kBwdThreads)) = v[h];
         }
     }
     // MFMA fragment of the 32 indices [base, base + 32) at k = kb .. kb + 15:
@@ -208,7 +229,8 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
     if (slot >= span) return;
     const int64_t tile = (int64_t)(blockIdx.x & 7) * span + slot;
     if (tile >= total) return;
-    int64_t m0, m_end, n0, k_begin, k_end, expert, row_end = 0;
+    int32_t m0, m_end, n0, k_begin, k_end, row_end = 0;
+    int64_t expert;
     if (!BY_EXPERT) {
         const int64_t mt = tile / P.n_tiles_n;
         const int4 d = P.mtiles[mt];
@@ -216,13 +238,13 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
         m_end = d.x + 32 * d.z;
         row_end = d.w;
         expert = d.y;
-        n0 = (tile % P.n_tiles_n) * TN;
+        n0 = (int32_t)(tile % P.n_tiles_n) * TN;
         k_begin = 0;
         k_end = P.Kd;
     } else {
         const int64_t per_e = (int64_t)P.n_tiles_m * P.n_tiles_n;
         expert = tile / per_e;
-        const int64_t rem = tile % per_e;
+        const int32_t rem = (int32_t)(tile % per_e);
         m0 = (rem / P.n_tiles_n) * kBwdTile;
         m_end = P.M;
         n0 = (rem % P.n_tiles_n) * kBwdTile;
@@ -232,16 +254,26 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
     const uint16_t* bbase = P.b + expert * P.b_estride;
     BwdLoad<!BY_EXPERT> la;
     BwdLoad<false, TN> lb;
-    // A: BY_EXPERT false, KC with memory rows m (sorted rows); true, MC with
-    // memory rows k (sorted rows).  B: MC with memory rows k -- an expert's
-    // weight rows, or sorted rows.
-    // fetch chunk k0: an MC operand looks up the chunk's rows first (a KC
-    // operand's rows are the tile's, looked up once)
-    auto fetch = [&](int64_t k0) {
-        if (BY_EXPERT) la.rows(P.a_gather, P.row2pair, P.top_k, m0, m_end, k0, k_end);
-        lb.rows(P.b_gather, P.row2pair, P.top_k, n0, P.N, k0, k_end);
-        la.fetch(P.a, P.lda, m0, m_end, k0, k_end);
-        lb.fetch(bbase, P.ldb, n0, P.N, k0, k_end);
+    // A: BY_EXPERT false, KC with memory rows m (sorted rows, or the tokens
+    // of dout's rows, looked up once per tile); true, MC with memory rows k
+    // (sorted rows, or their tokens).  B: MC with memory rows k -- an
+    // expert's weight rows, or sorted rows.  A gathered MC operand's row2pair
+    // entries are loaded a chunk ahead, so a chunk's data loads never wait
+    // for its lookups.
+    const bool ga = BY_EXPERT && P.a_gather, gb = P.b_gather;
+    auto prefetch_rows = [&](int32_t k0) {
+        if (ga) la.mc_prefetch(P.row2pair, k0, k_end);
+        if (gb) lb.mc_prefetch(P.row2pair, k0, k_end);
+    };
+    auto fetch = [&](int32_t k0) {
+        if (BY_EXPERT) {
+            if (ga) la.mc_gathered_rows(P.top_k);
+            else la.mc_rows(k0, k_end);
+        }
+        if (gb) lb.mc_gathered_rows(P.top_k);
+        else lb.mc_rows(k0, k_end);
+        la.fetch(P.a, P.lda, m0, m_end, k0);
+        lb.fetch(bbase, P.ldb, n0, P.N, k0);
     };
     f32x16 acc[NI][2];
 #pragma unroll
@@ -249,14 +281,23 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
 #pragma unroll
         for (int j = 0; j < 2; j++) acc[i][j] = f32x16{};
     const int r = lane & 31, kh = lane >> 5;
-    if (!BY_EXPERT) la.rows(P.a_gather, P.row2pair, P.top_k, m0, m_end, k_begin, k_end);
-    if (k_begin < k_end) fetch(k_begin);
-    for (int64_t k0 = k_begin; k0 < k_end; k0 += kBwdChunk) {
+    if (!BY_EXPERT) la.kc_rows(P.a_gather, P.row2pair, P.top_k, m0, m_end);
+    const bool mask_rows = !BY_EXPERT && m_end - m0 < kBwdTile;  // a row tile of fewer than 128 rows
+    if (k_begin < k_end) {
+        prefetch_rows(k_begin);
+        fetch(k_begin);
+        if (k_begin + kBwdChunk < k_end) prefetch_rows(k_begin + kBwdChunk);
+    }
+    for (int32_t k0 = k_begin; k0 < k_end; k0 += kBwdChunk) {
         __syncthreads();  // the previous chunk's fragments are read
-        la.store(SA);
-        lb.store(SB);
+        const bool mask_k = k0 + kBwdChunk > k_end;  // the last, partial chunk
+        la.store(SA, BY_EXPERT ? mask_k : mask_rows, m0, m_end, k0, k_end);
+        lb.store(SB, mask_k, n0, P.N, k0, k_end);
         __syncthreads();
-        if (k0 + kBwdChunk < k_end) fetch(k0 + kBwdChunk);  // next chunk in flight during the MFMAs
+        if (k0 + kBwdChunk < k_end) {  // next chunk in flight during the MFMAs
+            fetch(k0 + kBwdChunk);
+            if (k0 + 2 * kBwdChunk < k_end) prefetch_rows(k0 + 2 * kBwdChunk);
+        }
 #pragma unroll
         for (int ks = 0; ks < kBwdChunk / 16; ks++) {
             bf16x8b af[NI], bfr[2];
