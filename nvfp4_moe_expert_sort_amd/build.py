@@ -36,8 +36,10 @@ def _compile(src: str) -> str:
 
 
 # Stand-alone measurement programs (not part of the library): the GEMM path
-# comparison behind the choice of exact f16 dequantization.
-PROBES = {"mfma_path_probe": os.path.join(HERE, "probes", "mfma_path.hip")}
+# comparison behind the choice of exact f16 dequantization, and the L2 -> CU
+# read bandwidth of the GEMMs' operand-fetch patterns.
+PROBES = {"mfma_path_probe": os.path.join(HERE, "probes", "mfma_path.hip"),
+          "l2_patterns_probe": os.path.join(HERE, "probes", "l2_patterns.hip")}
 
 
 def _build_probe(item) -> str:
