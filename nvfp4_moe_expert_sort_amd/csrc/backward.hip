@@ -379,7 +379,8 @@ __global__ void __launch_bounds__(kBwdThreads, 2) bwd_gemm_kernel(BwdGemmParams 
 // dprob = FP32 sum of dh silu(gate) up, each lane over its columns in
 // increasing order, then a fixed butterfly.  silu and silu' use the hardware
 // exp2 and reciprocal: sig = 1 / (1 + e^-g), silu = g sig,
-// silu' = sig (1 + g (1 - sig)).
+// silu' = sig (1 + g (1 - sig)).  Lane l takes the 8 columns 8 l + 512 j
+// (16-byte loads and stores; I is a multiple of 128).
 __global__ void __launch_bounds__(256) swiglu_backward_kernel(const uint16_t* __restrict__ dh,
                                                               const uint16_t* __restrict__ y1, int64_t rows,
                                                               int32_t I, const int32_t* __restrict__ row2pair,
@@ -393,17 +394,33 @@ __global__ void __launch_bounds__(256) swiglu_backward_kernel(const uint16_t* __
     if (p < 0) return;
     const float pr = row_prob[r];
     float dp = 0.0f;
-    for (int n = lane; n < I; n += kWave) {
-        const float d = bf16_to_f32(dh[r * I + n]);
-        const float g = bf16_to_f32(y1[r * 2 * I + n]);
-        const float u = bf16_to_f32(y1[r * 2 * I + I + n]);
-        const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
-        const float s = g * sig;
-        const float ds = sig * (1.0f + g * (1.0f - sig));
-        const float dpr = d * pr;
-        dy1[r * 2 * I + n] = (uint16_t)bf16_hw(dpr * u * ds);
-        dy1[r * 2 * I + I + n] = (uint16_t)bf16_hw(dpr * s);
-        dp = dp + d * s * u;
+    for (int n0 = 8 * lane; n0 < I; n0 += 8 * kWave) {
+        const u32x4 dv = *reinterpret_cast<const u32x4*>(dh + r * I + n0);
+        const u32x4 gv = *reinterpret_cast<const u32x4*>(y1 + r * 2 * I + n0);
+        const u32x4 uv = *reinterpret_cast<const u32x4*>(y1 + r * 2 * I + I + n0);
+        u32x4 dg, du;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const int w = e >> 1, sh = 16 * (e & 1);
+            const float d = bf16_to_f32((uint16_t)(dv[w] >> sh));
+            const float g = bf16_to_f32((uint16_t)(gv[w] >> sh));
+            const float u = bf16_to_f32((uint16_t)(uv[w] >> sh));
+            const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+            const float sv = g * sig;
+            const float ds = sig * (1.0f + g * (1.0f - sig));
+            const float dpr = d * pr;
+            const uint32_t a = bf16_hw(dpr * u * ds), b = bf16_hw(dpr * sv);
+            if (e & 1) {
+                dg[w] |= a << 16;
+                du[w] |= b << 16;
+            } else {
+                dg[w] = a;
+                du[w] = b;
+            }
+            dp = dp + d * sv * u;
+        }
+        *reinterpret_cast<u32x4*>(dy1 + r * 2 * I + n0) = dg;
+        *reinterpret_cast<u32x4*>(dy1 + r * 2 * I + I + n0) = du;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) dp += __shfl_xor(dp, o, kWave);
