@@ -173,3 +173,17 @@ def test_backward_qwen3_layer(gpu, orc):
     """Qwen3-30B-A3B-shaped layer, 4096 tokens: every step of every pair."""
     m, dev = gpu
     _parity(m, orc, W.qwen3(seed=2), "qwen3 T=4096")
+
+
+def test_backward_skewed(gpu, orc):
+    """Zipf(1.1) expert popularity at the Qwen3 shape, T = 2048: the hottest
+    expert holds 1978 rows (weight-gradient K loops of 31 chunks, many row
+    tiles of one expert in dh and the FC1 input gradient) and 9 experts none
+    (their weight gradients are zeros)."""
+    m, dev = gpu
+    wl = W.skewed(seed=3, T=2048)
+    counts = wl.expert_counts()
+    assert counts.max() == 1978 and (counts == 0).sum() == 9
+    R = _parity(m, orc, wl, "skewed T=2048")
+    empty = np.nonzero(counts == 0)[0]
+    assert not R["dw1"][empty].any() and not R["dw2"][empty].any()
