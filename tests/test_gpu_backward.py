@@ -143,15 +143,18 @@ def _parity(m, orc, wl, label, T=None):
     return R
 
 
-@pytest.mark.parametrize("case", ["tiny", "H384_I384_E5_K5", "H256_I640_E3_K2"])
+SMALL_CASES = {
+    "H384_I384_E5_K5": W.MoEShape(T=37, H=384, E=5, K=5, I=384),  # every token to every expert
+    "H256_I640_E3_K2": W.MoEShape(T=450, H=256, E=3, K=2, I=640),  # a partial 256-column tile (640)
+    "H256_I256_E4_K1": W.MoEShape(T=300, H=256, E=4, K=1, I=256),  # top-1 routing
+    "H128_I128_E1_K1": W.MoEShape(T=200, H=128, E=1, K=1, I=128),  # one expert takes every token
+}
+
+
+@pytest.mark.parametrize("case", ["tiny", *SMALL_CASES])
 def test_backward_small(gpu, orc, case):
     m, dev = gpu
-    if case == "tiny":
-        wl = W.tiny(seed=0)
-    elif case == "H384_I384_E5_K5":
-        wl = W.MoEWorkload(case, 12, W.MoEShape(T=37, H=384, E=5, K=5, I=384))
-    else:
-        wl = W.MoEWorkload(case, 12, W.MoEShape(T=450, H=256, E=3, K=2, I=640))
+    wl = W.tiny(seed=0) if case == "tiny" else W.MoEWorkload(case, 12, SMALL_CASES[case])
     _parity(m, orc, wl, case)
 
 
