@@ -197,26 +197,39 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ x, i
     if (lane == 0) gout[r] = rs.g;
 }
 
-// One row per wavefront, held in registers: lane l owns the 32-element groups
-// l, l + 64, ... (G of them, cols <= 2048 G, cols % 32 == 0), so the row is
-// read once for its amax and its quantization.  Same arithmetic and outputs
-// as quant_row_wave.
 template <int G>
-__device__ __forceinline__ void quant_row_regs(const uint16_t* __restrict__ x, int64_t cols, bool round_up, bool gemm,
-                                               int64_t r, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                               float* __restrict__ gout) {
+struct RowRegs {
+    u32x4 v[G][4];
+};
+
+// The loads of quant_row_regs alone: lane l's groups l, l + 64, ... of the
+// row into registers (issued, not waited for).  No branch: a lane past the
+// row's last group re-reads that group (row_quant ignores it).
+template <int G>
+__device__ __forceinline__ void row_load(const uint16_t* __restrict__ x, int64_t cols, RowRegs<G>& rr) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t groups = cols >> 5;
-    u32x4 v[G][4];
+#pragma unroll
+    for (int gg = 0; gg < G; gg++) {
+        const int64_t gi = lane + kWave * gg;
+        load32(x + (gi < groups ? gi : groups - 1) * 32, false, rr.v[gg]);
+    }
+}
+
+// The rest of quant_row_regs on a row loaded by row_load.
+template <int G>
+__device__ __forceinline__ void row_quant(const RowRegs<G>& rr, int64_t cols, bool round_up, bool gemm, int64_t r,
+                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                          float* __restrict__ gout) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t groups = cols >> 5;
     uint32_t m = 0u;
 #pragma unroll
     for (int gg = 0; gg < G; gg++) {
         const int64_t gi = lane + kWave * gg;
-        if (gi < groups) {
-            load32(x + gi * 32, false, v[gg]);
-            m = max(m, max(max(absmax8_bits(v[gg][0]), absmax8_bits(v[gg][1])),
-                           max(absmax8_bits(v[gg][2]), absmax8_bits(v[gg][3]))));
-        }
+        if (gi < groups)
+            m = max(m, max(max(absmax8_bits(rr.v[gg][0]), absmax8_bits(rr.v[gg][1])),
+                           max(absmax8_bits(rr.v[gg][2]), absmax8_bits(rr.v[gg][3]))));
     }
     const RowScale rs = row_scale(bf16_to_f32(wave_max_u32(m)));
 #pragma unroll
@@ -225,7 +238,7 @@ __device__ __forceinline__ void quant_row_regs(const uint16_t* __restrict__ x, i
         if (gi < groups) {
             u32x4 c;
             uint32_t s2;
-            quant32(v[gg], rs, round_up, false, c, s2);
+            quant32(rr.v[gg], rs, round_up, false, c, s2);
             const int64_t k = gi * 32;
             if (gemm) {
                 *reinterpret_cast<u32x4*>(codes + gemm_code_off(r, k, cols)) = c;
@@ -237,6 +250,19 @@ __device__ __forceinline__ void quant_row_regs(const uint16_t* __restrict__ x, i
         }
     }
     if (lane == 0) gout[r] = rs.g;
+}
+
+// One row per wavefront, held in registers: lane l owns the 32-element groups
+// l, l + 64, ... (G of them, cols <= 2048 G, cols % 32 == 0), so the row is
+// read once for its amax and its quantization.  Same arithmetic and outputs
+// as quant_row_wave.
+template <int G>
+__device__ __forceinline__ void quant_row_regs(const uint16_t* __restrict__ x, int64_t cols, bool round_up, bool gemm,
+                                               int64_t r, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                               float* __restrict__ gout) {
+    RowRegs<G> rr;
+    row_load<G>(x, cols, rr);
+    row_quant<G>(rr, cols, round_up, gemm, r, codes, scales, gout);
 }
 
 // Several short rows per wavefront (cols % 32 == 0, at most LPR 32-element

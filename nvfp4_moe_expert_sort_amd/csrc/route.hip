@@ -46,7 +46,9 @@
 namespace nvfp4 {
 
 constexpr int kCountThreads = kTokPerBlk * 64;  // one wavefront per token of the block
+constexpr int kRouteWaitLgkm0 = 0xC07F;         // s_waitcnt lgkmcnt(0)
 
+template <bool QX>  // X quantized here (false: BF16 activations, the W4A16 variant)
 __global__ void __launch_bounds__(kCountThreads) route_count_kernel(const uint16_t* __restrict__ x,
                                                                     const int32_t* __restrict__ ids, int32_t T,
                                                                     int32_t H, int32_t K, int32_t E, int round_up,
@@ -61,27 +63,45 @@ __global__ void __launch_bounds__(kCountThreads) route_count_kernel(const uint16
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t t0 = (int64_t)blockIdx.x * kTokPerBlk;
     for (int e = tid; e < E; e += kCountThreads) cnt[e] = 0;
+    // Wave 0 ranks the block's pairs.  It loads their expert ids before its
+    // own token row, so that the row's loads are in flight while it ranks
+    // (a wave's loads return in order).
+    constexpr int kGroups = kTokPerBlk * kMaxTopK / kWave;  // groups of 64 pairs a block can hold
+    const int64_t p0 = t0 * K, p1 = min((t0 + kTokPerBlk) * K, (int64_t)T * K);
     __syncthreads();
+    int32_t eg[kGroups];
     if (wave == 0) {
+#pragma unroll
+        for (int g = 0; g < kGroups; g++) {
+            const int64_t p = p0 + (int64_t)g * kWave + lane;
+            eg[g] = p < p1 ? ids[p] : -1;
+        }
+    }
+    auto rank = [&]() {
+        if (wave != 0) return;
         // Stable ranks in pair order: pairs are taken 64 at a time; lanes with
         // the same expert find each other with one ballot per id bit.
-        const int64_t p0 = t0 * K, p1 = min((t0 + kTokPerBlk) * K, (int64_t)T * K);
         int nbits = 0;
         while ((1 << nbits) < E) nbits++;
         int err = 0;
-        for (int64_t c0 = p0; c0 < p1; c0 += kWave) {
+#pragma unroll
+        for (int g = 0; g < kGroups; g++) {
+            const int64_t c0 = p0 + (int64_t)g * kWave;
+            if (c0 >= p1) break;
             const int64_t p = c0 + lane;
-            const int32_t e = p < p1 ? ids[p] : -1;
+            const int32_t e = eg[g];
             const bool valid = e >= 0 && e < E;
             if (p < p1 && !valid) err |= 1;
             // A token may not name an expert twice: compare with the token's
-            // earlier slots, taken from the lanes that hold them (or memory
-            // when the token began in the previous group of 64).
+            // earlier slots, taken from the lanes that hold them (in the
+            // previous group when the token began there; a block starts at a
+            // token, so group 0 never looks back).
             const int kk = (int)((uint32_t)p % (uint32_t)K);  // pair indices are < 2^30
             for (int d = 1; d < K; d++) {
                 const int32_t ed = __shfl(e, max(lane - d, 0), kWave);
+                const int32_t ep = __shfl(eg[g > 0 ? g - 1 : 0], (lane - d + kWave) & (kWave - 1), kWave);
                 if (valid && d <= kk) {
-                    const int32_t prev = lane >= d ? ed : ids[p - d];
+                    const int32_t prev = lane >= d ? ed : ep;
                     if (prev == e) err |= 2;
                 }
             }
@@ -94,7 +114,7 @@ __global__ void __launch_bounds__(kCountThreads) route_count_kernel(const uint16
             const uint64_t below = mask & ((1ull << lane) - 1ull);
             int32_t rank = -1;
             if (valid) rank = cnt[e] + __popcll(below);
-            __builtin_amdgcn_s_waitcnt(0);  // every lane's read of cnt[] precedes the leaders' updates
+            __builtin_amdgcn_s_waitcnt(kRouteWaitLgkm0);  // every lane's read of cnt[] precedes the leaders' updates
             __builtin_amdgcn_wave_barrier();
             if (valid && below == 0ull) cnt[e] += __popcll(mask);
             if (p < p1) lrank[p] = rank;
@@ -102,20 +122,39 @@ __global__ void __launch_bounds__(kCountThreads) route_count_kernel(const uint16
         // OR the lanes' error bits
         for (int o = 32; o > 0; o >>= 1) err |= __shfl_xor(err, o, kWave);
         if (lane == 0) blk_err[blockIdx.x] = err;
-    }
-    // Each wave quantizes its token's row once (amax in the same pass).
+    };
+    // Each wave quantizes its token's row once (amax in the same pass).  The
+    // row's loads are issued without a branch (a wave past the last token
+    // loads the last row and stores nothing), so the rank's waits for the ids
+    // count in order past them instead of waiting for everything.
     const int64_t t = t0 + wave;
-    if (quant_x && t < T) {
-        const int64_t groups_per_lane = (H / 32 + kWave - 1) / kWave;
-        const uint16_t* xr = x + t * H;
-        const bool ru = round_up != 0;
-        switch (groups_per_lane) {
-            case 1: quant_row_regs<1>(xr, H, ru, false, t, xq_codes, xq_scales, gx); break;
-            case 2: quant_row_regs<2>(xr, H, ru, false, t, xq_codes, xq_scales, gx); break;
-            case 3: quant_row_regs<3>(xr, H, ru, false, t, xq_codes, xq_scales, gx); break;
-            case 4: quant_row_regs<4>(xr, H, ru, false, t, xq_codes, xq_scales, gx); break;
-            default: quant_row_wave(xr, H, -1.0f, ru, false, t, xq_codes, xq_scales, gx); break;
-        }
+    const bool qx = QX && quant_x && t < T;
+    int64_t groups_per_lane = (H / 32 + kWave - 1) / kWave;
+    const uint16_t* xr = x + (t < T ? t : T - 1) * H;
+    const bool ru = round_up != 0;
+    if (!QX) {
+        rank();
+        groups_per_lane = 0;  // no quantization
+    }
+    switch (groups_per_lane) {
+        case 0: break;
+#define NVFP4_ROUTE_COUNT_CASE(G)                                                 \
+    case G: {                                                                     \
+        RowRegs<G> rr;                                                            \
+        row_load<G>(xr, H, rr);                                                   \
+        rank();                                                                   \
+        if (qx) row_quant<G>(rr, H, ru, false, t, xq_codes, xq_scales, gx);       \
+        break;                                                                    \
+    }
+        NVFP4_ROUTE_COUNT_CASE(1)
+        NVFP4_ROUTE_COUNT_CASE(2)
+        NVFP4_ROUTE_COUNT_CASE(3)
+        NVFP4_ROUTE_COUNT_CASE(4)
+#undef NVFP4_ROUTE_COUNT_CASE
+        default:
+            rank();
+            if (qx) quant_row_wave(xr, H, -1.0f, ru, false, t, xq_codes, xq_scales, gx);
+            break;
     }
     __syncthreads();
     for (int e = tid; e < E; e += kCountThreads) blk_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
@@ -502,10 +541,9 @@ hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* prob
         if (st != hipSuccess) return st;
     } else {
     const int32_t nblk = (T + kTokPerBlk - 1) / kTokPerBlk;
-    hipLaunchKernelGGL(route_count_kernel, dim3(nblk), dim3(kCountThreads), 0, stream, x, ids, T, H, K, E, round_up ? 1 : 0,
-                       quant_x ? 1 : 0,
-                       rb.blk_counts, rb.blk_err, rb.pair2row /* holds the ranks until route_place */, rb.xq_codes,
-                       rb.xq_scales, rb.gx);
+    hipLaunchKernelGGL(quant_x ? route_count_kernel<true> : route_count_kernel<false>, dim3(nblk), dim3(kCountThreads),
+                       0, stream, x, ids, T, H, K, E, round_up ? 1 : 0, quant_x ? 1 : 0, rb.blk_counts, rb.blk_err,
+                       rb.pair2row /* holds the ranks until route_place */, rb.xq_codes, rb.xq_scales, rb.gx);
     st = hipGetLastError();
     if (st != hipSuccess) return st;
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, nblk, E, capacity, rb.blk_counts, rb.blk_err,
