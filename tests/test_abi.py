@@ -112,6 +112,37 @@ def test_forward_host_validation(m):
     assert f(ctypes.byref(cfg), None, 0, None, None, ctypes.byref(W1), ctypes.byref(W2), None, fake, need, None) == 0
 
 
+def test_backward_host_validation(m):
+    """nvfp4moe_moe_expert_backward rejects bad arguments on the host, before
+    launching anything, with the forward's error codes."""
+    lib = m.lib()
+    cfg = _cfg(m, max_tokens=64)
+    rows = int(m.workspace_layout(cfg).rows_cap)
+    fwd = m.workspace_bytes(cfg)
+    need = lib.nvfp4moe_backward_workspace_bytes(ctypes.byref(cfg))
+    assert need > 0 and need % 256 == 0
+    assert lib.nvfp4moe_backward_workspace_bytes(ctypes.byref(_cfg(m, max_tokens=128))) > need
+    assert lib.nvfp4moe_backward_workspace_bytes(ctypes.byref(_cfg(m, hidden=100))) == 0
+    f = lib.nvfp4moe_moe_expert_backward
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+    def call(cfgp=ctypes.byref(cfg), x=fake, T=1, y1_rows=rows, fw=fake, fw_bytes=fwd, ws=fake, ws_bytes=need,
+             dprobs=fake, dout=fake):
+        return f(cfgp, x, T, fake, fake, fake, y1_rows, fw, fw_bytes, dout, fake, dprobs, fake, fake, ws, ws_bytes,
+                 None)
+
+    assert call(cfgp=None) == 1                             # null config
+    assert call(cfgp=ctypes.byref(_cfg(m, hidden=100))) == 2  # bad config
+    assert call(T=-1) == 2 and call(T=65) == 5              # negative T, T past max_tokens
+    assert call(y1_rows=rows - 1) == 2                      # y1 shorter than the sorted rows
+    assert call(fw=None) == 1 and call(ws=None) == 1        # null workspaces
+    assert call(fw_bytes=fwd - 1) == 4 and call(ws_bytes=need - 1) == 4
+    assert call(fw=ctypes.c_void_p(0x1010)) == 3 and call(ws=ctypes.c_void_p(0x1080)) == 3
+    assert call(T=0, x=None, dout=None, dprobs=None) == 0   # T == 0 launches nothing
+    assert call(x=None) == 1 and call(dout=None) == 1       # null tensors with T > 0
+    assert call(x=ctypes.c_void_p(0x1002)) == 3 and call(dprobs=ctypes.c_void_p(0x1002)) == 3
+
+
 def test_masked_layout_sizes_and_host_validation(m):
     """Masked fixed-capacity layout: E chunks of `capacity` rows (a positive
     multiple of 32), checked on the host before anything is launched."""
