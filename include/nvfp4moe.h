@@ -239,6 +239,23 @@ NVFP4MOE_API int nvfp4moe_moe_expert_forward_w4a16(const nvfp4moe_config* cfg, c
                                                    const nvfp4_qtensor* W2q, uint16_t* out, void* workspace,
                                                    size_t workspace_bytes, void* stream);
 
+/* The expert forward with the activations' max, quantization and FC1 GEMM
+ * fused (miniTE summary page, "assumptions and limits": the online
+ * amax-quantization-GEMM fusion, whose numerical and performance validation
+ * the page leaves open).  The sort records each token's max |x| instead of a
+ * quantized copy of X (no gather); FC1 loads each sorted row's BF16 token
+ * row and quantizes it as it goes, 32 elements per lane, with the outer scale
+ * g = max|x| / 2688, the E4M3 block scales (cfg->scale_round) and the E2M1
+ * codes of nvfp4moe_moe_expert_forward's quantizer, so every output is
+ * bitwise that entry point's.  g is known before the GEMM starts (the sort
+ * takes the max over the whole row), so no accumulator is ever rescaled.
+ * Same arguments, workspace and errors as nvfp4moe_moe_expert_forward;
+ * contiguous row layout only; no synchronisation. */
+NVFP4MOE_API int nvfp4moe_moe_expert_forward_online(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T,
+                                                    const int32_t* ids, const float* probs, const nvfp4_qtensor* W1q,
+                                                    const nvfp4_qtensor* W2q, uint16_t* out, void* workspace,
+                                                    size_t workspace_bytes, void* stream);
+
 /* The same forward, recording caller-created hipEvent_t events[i] on `stream`
  * at each stage boundary, for timing the stages inside a timed region
  * (events[0] before the sort, [1] after the sort and the quantization of X,

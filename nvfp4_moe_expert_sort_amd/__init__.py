@@ -30,7 +30,7 @@ EXPORTS = ["nvfp4_status_str", "nvfp4_quantize", "nvfp4moe_weight_bytes", "nvfp4
            "nvfp4moe_workspace_layout", "nvfp4moe_workspace_bytes_masked", "nvfp4moe_workspace_layout_masked",
            "nvfp4moe_moe_expert_forward_masked", "nvfp4moe_moe_expert_forward_unfused",
            "nvfp4moe_moe_expert_forward_noalloc", "nvfp4moe_backward_workspace_bytes", "nvfp4moe_moe_expert_backward",
-           "nvfp4moe_moe_expert_forward_w4a16", "nvfp4moe_router_topk", "nvfp4_linear_workspace_bytes", "nvfp4_linear",
+           "nvfp4moe_moe_expert_forward_w4a16", "nvfp4moe_moe_expert_forward_online", "nvfp4moe_router_topk", "nvfp4_linear_workspace_bytes", "nvfp4_linear",
            "nvfp4moe_selftest_batch_invariance"]
 
 
@@ -86,6 +86,7 @@ def lib():
         "nvfp4moe_workspace_layout_masked": (ctypes.c_int, [cfgp, i32, ctypes.POINTER(WsLayout)]),
         "nvfp4moe_moe_expert_forward_masked": (ctypes.c_int, [cfgp, i32, vp, i32, vp, vp, qtp, qtp, vp, vp, sz, vp]),
         "nvfp4moe_moe_expert_forward_w4a16": (ctypes.c_int, [cfgp, vp, i32, vp, vp, qtp, qtp, vp, vp, sz, vp]),
+        "nvfp4moe_moe_expert_forward_online": (ctypes.c_int, [cfgp, vp, i32, vp, vp, qtp, qtp, vp, vp, sz, vp]),
         "nvfp4moe_backward_workspace_bytes": (sz, [cfgp]),
         "nvfp4moe_moe_expert_backward": (ctypes.c_int, [cfgp, vp, i32, vp, vp, vp, i64, vp, sz, vp, vp, vp, vp, vp, vp,
                                                          sz, vp]),
@@ -236,6 +237,19 @@ def moe_expert_forward_w4a16(cfg: Config, x, ids, probs, weights: QuantWeights, 
                                                  ctypes.byref(weights.W1q), ctypes.byref(weights.W2q), _ptr(out),
                                                  _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "nvfp4moe_moe_expert_forward_w4a16")
+    return out
+
+
+def moe_expert_forward_online(cfg: Config, x, ids, probs, weights: QuantWeights, workspace, out=None, stream=None):
+    """nvfp4moe_moe_expert_forward_online: moe_expert_forward with X quantized inside FC1 (same output bits)."""
+    import torch
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, cfg.hidden), dtype=x.dtype, device=x.device)
+    st = lib().nvfp4moe_moe_expert_forward_online(ctypes.byref(cfg), _ptr(x), T, _ptr(ids), _ptr(probs),
+                                                  ctypes.byref(weights.W1q), ctypes.byref(weights.W2q), _ptr(out),
+                                                  _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "nvfp4moe_moe_expert_forward_online")
     return out
 
 

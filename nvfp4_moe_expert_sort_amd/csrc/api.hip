@@ -257,7 +257,7 @@ namespace {
 int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids, const float* probs,
                  const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q, uint16_t* out, void* workspace,
                  size_t workspace_bytes, void* stream, void* const* events, int32_t capacity = 0,
-                 bool w4a16 = false, uint16_t* y1 = nullptr) {
+                 bool w4a16 = false, uint16_t* y1 = nullptr, bool online = false) {
     if (!cfg) return NVFP4_E_NULL;
     if (!cfg_ok(cfg)) return NVFP4_E_SHAPE;
     if (capacity != 0 && !capacity_ok(cfg, capacity)) return NVFP4_E_SHAPE;
@@ -301,7 +301,7 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
 
     if (!mark(0)) return NVFP4_E_HIP;
     hipError_t e = launch_route(x, ids, probs, T, (int32_t)H, (int32_t)K, (int32_t)E, capacity, ru, rb, L.pub.rows_cap, s,
-                                !w4a16);
+                                !w4a16, online);
     if (e != hipSuccess || !mark(1)) return NVFP4_E_HIP;
 
     // Static bounds for this T (the device counts are <= these): at most
@@ -369,6 +369,15 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
     f1.amax_part = (float*)(ws + L.pub.amax2_part);
     f1.n_part = (int32_t)(I / 32);
     f1.inter = (int32_t)I;
+    if (online) {
+        // X quantized inside FC1 from its BF16 rows (the sort recorded each
+        // token's max |x| in gx and each sorted row's g in a1_g)
+        f1.a_bf16 = x;
+        f1.a_amax = rb.gx;
+        f1.a_row2pair = rb.row2pair;
+        f1.a_top_k = (int32_t)K;
+        f1.a_round_up = ru ? 1 : 0;
+    }
     if (y1) {
         // Unfused: y1 = bf16(acc * g^x * g^w1) for all 2I weight rows (the
         // plain epilogue, whose arithmetic per element is the fused one's),
@@ -398,7 +407,7 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
         const int64_t fc1_tiles = mt_bound * f1.n_tiles_n;
         const bool hybrid = fc1_tiles > 2 * (int64_t)hybrid_persist();
         f1.persist = hybrid ? hybrid_persist() : 0;
-        e = launch_gemm(kGemmSwiGLU, f1, hybrid ? hybrid_grid(fc1_tiles) : (int)fc1_tiles, s);
+        e = launch_gemm(kGemmSwiGLU, f1, hybrid ? hybrid_grid(fc1_tiles) : (int)fc1_tiles, s, online);
         if (e != hipSuccess || !mark(2)) return NVFP4_E_HIP;
     }
 
@@ -443,6 +452,13 @@ int nvfp4moe_moe_expert_forward(const nvfp4moe_config* cfg, const uint16_t* x, i
                                 const float* probs, const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q,
                                 uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
     return forward_impl(cfg, x, T, ids, probs, W1q, W2q, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int nvfp4moe_moe_expert_forward_online(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids,
+                                       const float* probs, const nvfp4_qtensor* W1q, const nvfp4_qtensor* W2q,
+                                       uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+    return forward_impl(cfg, x, T, ids, probs, W1q, W2q, out, workspace, workspace_bytes, stream, nullptr, 0, false,
+                        nullptr, true);
 }
 
 int nvfp4moe_moe_expert_forward_events(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const int32_t* ids,

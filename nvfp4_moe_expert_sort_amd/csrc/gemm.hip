@@ -45,6 +45,7 @@
 //    size: a row's bits depend only on its own inputs.
 #include "nvfp4_device.h"
 #include "nvfp4_kernels.h"
+#include "nvfp4_quant_row.h"
 
 namespace nvfp4 {
 
@@ -99,7 +100,9 @@ __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(
 // ADEC false: this wave has no activation subtile of its own (wave >= NSUB)
 // and is compiled without the K loop's activation decodes; the choice is made
 // once per tile by a wave-uniform branch, so the MFMA stream has no branch.
-template <int MODE, int NSUB, bool ADEC>
+// AQ true (FC1 only): the activations arrive in BF16 and are quantized here,
+// one 32-element group per lane and chunk, just before their decode.
+template <int MODE, int NSUB, bool ADEC, bool AQ>
 __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, SharedB& SB, int32_t row0, int32_t expert,
                                            int32_t row_end, int32_t nt) {
     // wave index as a scalar, so per-wave conditions are scalar branches
@@ -138,6 +141,32 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
 
     const uint8_t* a_c = P.a_codes + lane * 16;
     const uint8_t* a_s = P.a_scales + lane * 4;
+
+    // AQ: lane l of wave `ai` owns row row0 + 32 ai + l % 32 and, in every
+    // 64-column chunk, the 32 columns of half l / 32 -- exactly the GEMM
+    // layout's 16-byte unit of that lane -- which it quantizes with the
+    // library's 32-element quantizer against its token's outer scale: the
+    // codes and scales the sort's quantizer and gather put in that unit.
+    const uint16_t* xrow = P.a_bf16;
+    RowScale rsa{0.0f, 0.0f, true};
+    if (AQ && ADEC) {
+        const int32_t arow = row0 + 32 * ai + (lane & 31);
+        const int32_t pr = P.a_row2pair[arow];
+        // padding rows read token 0 (their results are never stored)
+        const int64_t tok = pr >= 0 ? (int64_t)((uint32_t)pr / (uint32_t)P.a_top_k) : 0;
+        rsa = row_scale(P.a_amax[tok]);
+        xrow = P.a_bf16 + tok * K + 32 * (lane >> 5);
+    }
+    auto load_xa = [&](int64_t cp, u32x4 (&vb)[2][4]) {
+#pragma unroll
+        for (int ch = 0; ch < 2; ch++) load32(xrow + 128 * cp + 64 * ch, false, vb[ch]);
+    };
+    // chunk ch's codes into xa, its two block scales into bytes 2ch, 2ch + 1 of ya
+    auto quant_xa = [&](int ch, const u32x4 (&vb)[4], u32x4& xa, uint32_t& ya) {
+        uint32_t s2;
+        quant32(vb, rsa, P.a_round_up != 0, false, xa, s2);
+        ya = ch == 0 ? s2 : (ya | (s2 << 16));
+    };
     const uint8_t* b_c = P.b_codes + lane * 16;
     const uint8_t* b_s = P.b_scales + lane * 4;
 
@@ -197,9 +226,18 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
     u32x4 ub[2][2];  // this step's weight codes [chunk][column tile]
     uint32_t usb[2];
     {
-        u32x4 ua[2];
-        uint32_t usa;
-        load_a(0, ua, usa);
+        u32x4 ua[2] = {};
+        uint32_t usa = 0u;
+        if (AQ) {
+            if (ADEC) {
+                u32x4 vb[2][4];
+                load_xa(0, vb);
+                quant_xa(0, vb[0], ua[0], usa);
+                quant_xa(1, vb[1], ua[1], usa);
+            }
+        } else {
+            load_a(0, ua, usa);
+        }
 #pragma unroll
         for (int ch = 0; ch < 2; ch++)
 #pragma unroll
@@ -219,7 +257,12 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
         const int64_t cpn = more ? cp + 1 : cp;
         u32x4 na[2];
         uint32_t nsa, nsb[2];
-        load_a(cpn, na, nsa);
+        u32x4 nv[2][4];  // AQ: the next step's BF16 activations
+        if (AQ) {
+            if (ADEC) load_xa(cpn, nv);
+        } else {
+            load_a(cpn, na, nsa);
+        }
         load_bs(cpn, nsb);
         if (active) {
             half2v bsc[2][2][2];  // [chunk][column tile][lo/hi]
@@ -252,6 +295,10 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(acur[i], bv[j], acc[i][j], 0, 0, 0);
 #pragma unroll
                 for (int j = 0; j < 2; j++) bn[j] = decode8(ub[chn][j][ksn], bsc[chn][j][ksn >> 1]);
+                // AQ: the next step's activations quantized on k-steps 2 and 3
+                // (one chunk each), ahead of their decode on k-steps 4..7
+                if (AQ && ADEC && st == 2) quant_xa(0, nv[0], na[0], nsa);
+                if (AQ && ADEC && st == 3) quant_xa(1, nv[1], na[1], nsa);
                 if (st < 7) {
 #pragma unroll
                     for (int i = 0; i < NSUB; i++) acur[i] = anxt[i];
@@ -292,6 +339,10 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
                 for (int j = 0; j < 2; j++) bv[j] = bn[j];
             }
         } else {
+            if (AQ && ADEC) {
+                quant_xa(0, nv[0], na[0], nsa);
+                quant_xa(1, nv[1], na[1], nsa);
+            }
             decode_a(buf ^ 1, na, nsa);
         }
         // Step cp+1's weight codes: landed in LDS (wait for this wave's
@@ -430,7 +481,7 @@ __device__ __forceinline__ void block_tile(const GemmParams& P, SharedA& S, Shar
     }
 }
 
-template <int MODE>
+template <int MODE, bool AQ = false>
 __global__ void __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_kernel(GemmParams P) {
     __shared__ SharedA S;
@@ -478,24 +529,24 @@ gemm_kernel(GemmParams P) {
         if (t + per < t_end) d = tile_desc(t + per);
         const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
         switch (cur.z) {
-            case 4: block_tile<MODE, 4, true>(P, S, SB, cur.x, cur.y, cur.w, nt); break;
+            case 4: block_tile<MODE, 4, true, AQ>(P, S, SB, cur.x, cur.y, cur.w, nt); break;
             case 3:
                 if (wv < 3)
-                    block_tile<MODE, 3, true>(P, S, SB, cur.x, cur.y, cur.w, nt);
+                    block_tile<MODE, 3, true, AQ>(P, S, SB, cur.x, cur.y, cur.w, nt);
                 else
-                    block_tile<MODE, 3, false>(P, S, SB, cur.x, cur.y, cur.w, nt);
+                    block_tile<MODE, 3, false, AQ>(P, S, SB, cur.x, cur.y, cur.w, nt);
                 break;
             case 2:
                 if (wv < 2)
-                    block_tile<MODE, 2, true>(P, S, SB, cur.x, cur.y, cur.w, nt);
+                    block_tile<MODE, 2, true, AQ>(P, S, SB, cur.x, cur.y, cur.w, nt);
                 else
-                    block_tile<MODE, 2, false>(P, S, SB, cur.x, cur.y, cur.w, nt);
+                    block_tile<MODE, 2, false, AQ>(P, S, SB, cur.x, cur.y, cur.w, nt);
                 break;
             default:
                 if (wv < 1)
-                    block_tile<MODE, 1, true>(P, S, SB, cur.x, cur.y, cur.w, nt);
+                    block_tile<MODE, 1, true, AQ>(P, S, SB, cur.x, cur.y, cur.w, nt);
                 else
-                    block_tile<MODE, 1, false>(P, S, SB, cur.x, cur.y, cur.w, nt);
+                    block_tile<MODE, 1, false, AQ>(P, S, SB, cur.x, cur.y, cur.w, nt);
                 break;
         }
         barrier_lds();  // the next tile's prologue overwrites LDS buffer 0
@@ -504,9 +555,11 @@ gemm_kernel(GemmParams P) {
 
 int gemm_cols_per_tile(int mode) { return mode == kGemmSwiGLU ? 128 : 256; }
 
-hipError_t launch_gemm(int mode, const GemmParams& P, int grid_blocks, hipStream_t stream) {
+hipError_t launch_gemm(int mode, const GemmParams& P, int grid_blocks, hipStream_t stream, bool aq) {
     const int g = (grid_blocks + 7) / 8 * 8;
-    if (mode == kGemmSwiGLU)
+    if (mode == kGemmSwiGLU && aq)
+        hipLaunchKernelGGL((gemm_kernel<kGemmSwiGLU, true>), dim3(g), dim3(kThreads), 0, stream, P);
+    else if (mode == kGemmSwiGLU)
         hipLaunchKernelGGL(gemm_kernel<kGemmSwiGLU>, dim3(g), dim3(kThreads), 0, stream, P);
     else
         hipLaunchKernelGGL(gemm_kernel<kGemmPlain>, dim3(g), dim3(kThreads), 0, stream, P);

@@ -34,6 +34,15 @@ struct GemmParams {
     float* amax_part;          // SwiGLU mode: [rows][n_part] max |h| of each 32-column group
     int32_t n_part;            // SwiGLU mode: I / 32
     int32_t inter;             // SwiGLU mode: I (gate rows [0, I), up rows [I, 2I))
+    // Activations quantized inside the GEMM (gemm_kernel<kGemmSwiGLU, true>):
+    // row r's A operand is its token's BF16 row a_bf16[row2pair[r] / top_k]
+    // (K wide), quantized with the outer scale of a_amax[token] (max |x|);
+    // a_g[r] holds that row's g.
+    const uint16_t* a_bf16;
+    const float* a_amax;
+    const int32_t* a_row2pair;
+    int32_t a_top_k;
+    int32_t a_round_up;
 };
 
 struct RouteBuffers {
@@ -68,7 +77,7 @@ hipError_t launch_quant_h(const uint16_t* h, int64_t rows_bound, int64_t I, cons
 // variant reads the BF16 rows of x itself).
 hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* probs, int32_t T, int32_t H, int32_t K,
                         int32_t E, int32_t capacity, bool round_up, const RouteBuffers& rb, int64_t rows_cap,
-                        hipStream_t stream, bool quant_x = true);
+                        hipStream_t stream, bool quant_x = true, bool online = false);
 
 // W4A16 grouped GEMM (NVFP4 weights, BF16 activations): one workgroup per
 // (32-row subtile of a row tile, column tile).
@@ -140,7 +149,7 @@ struct BwdArgs {
 hipError_t launch_moe_backward(const BwdArgs& args, hipStream_t stream);
 
 int gemm_cols_per_tile(int mode);  // output columns per tile: 256 (plain) or 128 of h (128 gate + 128 up rows)
-hipError_t launch_gemm(int mode, const GemmParams& P, int grid_blocks, hipStream_t stream);
+hipError_t launch_gemm(int mode, const GemmParams& P, int grid_blocks, hipStream_t stream, bool aq = false);
 // The router-weighted SwiGLU producer on its own (unfused forward): h and the
 // per-32-column maxima of |h| from y1 [rows, 2I] (gate | up), for sorted rows
 // below min(rows_bound, expert_off[E]) that hold a pair.

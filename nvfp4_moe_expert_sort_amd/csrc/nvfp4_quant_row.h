@@ -197,6 +197,21 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ x, i
     if (lane == 0) gout[r] = rs.g;
 }
 
+// max |x| over a row of cols (cols % 16 == 0) BF16 values, one wavefront
+// (quant_row_wave's first pass).
+__device__ __forceinline__ float row_amax_wave(const uint16_t* __restrict__ x, int64_t cols) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t groups = (cols + 31) >> 5;
+    uint32_t m = 0u;
+    for (int64_t gi = lane; gi < groups; gi += kWave) {
+        const bool one = (gi + 1) * 32 > cols;
+        u32x4 v[4];
+        load32(x + gi * 32, one, v);
+        m = max(m, max(max(absmax8_bits(v[0]), absmax8_bits(v[1])), max(absmax8_bits(v[2]), absmax8_bits(v[3]))));
+    }
+    return bf16_to_f32(wave_max_u32(m));
+}
+
 template <int G>
 struct RowRegs {
     u32x4 v[G][4];
@@ -216,11 +231,9 @@ __device__ __forceinline__ void row_load(const uint16_t* __restrict__ x, int64_t
     }
 }
 
-// The rest of quant_row_regs on a row loaded by row_load.
+// max |x| over a row loaded by row_load (a BF16 value, exact in FP32).
 template <int G>
-__device__ __forceinline__ void row_quant(const RowRegs<G>& rr, int64_t cols, bool round_up, bool gemm, int64_t r,
-                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                          float* __restrict__ gout) {
+__device__ __forceinline__ float row_amax(const RowRegs<G>& rr, int64_t cols) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t groups = cols >> 5;
     uint32_t m = 0u;
@@ -231,7 +244,17 @@ __device__ __forceinline__ void row_quant(const RowRegs<G>& rr, int64_t cols, bo
             m = max(m, max(max(absmax8_bits(rr.v[gg][0]), absmax8_bits(rr.v[gg][1])),
                            max(absmax8_bits(rr.v[gg][2]), absmax8_bits(rr.v[gg][3]))));
     }
-    const RowScale rs = row_scale(bf16_to_f32(wave_max_u32(m)));
+    return bf16_to_f32(wave_max_u32(m));
+}
+
+// The rest of quant_row_regs on a row loaded by row_load.
+template <int G>
+__device__ __forceinline__ void row_quant(const RowRegs<G>& rr, int64_t cols, bool round_up, bool gemm, int64_t r,
+                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                          float* __restrict__ gout) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t groups = cols >> 5;
+    const RowScale rs = row_scale(row_amax<G>(rr, cols));
 #pragma unroll
     for (int gg = 0; gg < G; gg++) {
         const int64_t gi = lane + kWave * gg;

@@ -48,7 +48,12 @@ namespace nvfp4 {
 constexpr int kCountThreads = kTokPerBlk * 64;  // one wavefront per token of the block
 constexpr int kRouteWaitLgkm0 = 0xC07F;         // s_waitcnt lgkmcnt(0)
 
-template <bool QX>  // X quantized here (false: BF16 activations, the W4A16 variant)
+// What route_count does with X besides the sort: nothing (BF16 activations,
+// the W4A16 variant), quantize each token row (token-major Xq, g in gx), or
+// only its max |x| into gx (the forward that quantizes X inside FC1).
+constexpr int kXNone = 0, kXQuant = 1, kXAmax = 2;
+
+template <int XM>
 __global__ void __launch_bounds__(kCountThreads) route_count_kernel(const uint16_t* __restrict__ x,
                                                                     const int32_t* __restrict__ ids, int32_t T,
                                                                     int32_t H, int32_t K, int32_t E, int round_up,
@@ -128,13 +133,13 @@ __global__ void __launch_bounds__(kCountThreads) route_count_kernel(const uint16
     // loads the last row and stores nothing), so the rank's waits for the ids
     // count in order past them instead of waiting for everything.
     const int64_t t = t0 + wave;
-    const bool qx = QX && quant_x && t < T;
+    const bool qx = XM != kXNone && t < T;
     int64_t groups_per_lane = (H / 32 + kWave - 1) / kWave;
     const uint16_t* xr = x + (t < T ? t : T - 1) * H;
     const bool ru = round_up != 0;
-    if (!QX) {
+    if (XM == kXNone) {
         rank();
-        groups_per_lane = 0;  // no quantization
+        groups_per_lane = 0;  // nothing to read
     }
     switch (groups_per_lane) {
         case 0: break;
@@ -143,7 +148,11 @@ __global__ void __launch_bounds__(kCountThreads) route_count_kernel(const uint16
         RowRegs<G> rr;                                                            \
         row_load<G>(xr, H, rr);                                                   \
         rank();                                                                   \
-        if (qx) row_quant<G>(rr, H, ru, false, t, xq_codes, xq_scales, gx);       \
+        if (XM == kXQuant && qx) row_quant<G>(rr, H, ru, false, t, xq_codes, xq_scales, gx); \
+        if (XM == kXAmax) {                                                       \
+            const float am = row_amax<G>(rr, H);                                  \
+            if (qx && lane == 0) gx[t] = am;                                      \
+        }                                                                         \
         break;                                                                    \
     }
         NVFP4_ROUTE_COUNT_CASE(1)
@@ -153,7 +162,11 @@ __global__ void __launch_bounds__(kCountThreads) route_count_kernel(const uint16
 #undef NVFP4_ROUTE_COUNT_CASE
         default:
             rank();
-            if (qx) quant_row_wave(xr, H, -1.0f, ru, false, t, xq_codes, xq_scales, gx);
+            if (XM == kXQuant && qx) quant_row_wave(xr, H, -1.0f, ru, false, t, xq_codes, xq_scales, gx);
+            if (XM == kXAmax) {
+                const float am = row_amax_wave(xr, H);
+                if (qx && lane == 0) gx[t] = am;
+            }
             break;
     }
     __syncthreads();
@@ -433,11 +446,14 @@ __global__ void __launch_bounds__(kSmallWaves * 64) route_small_kernel(const uin
 
 // pair2row[p] holds the pair's rank within (its block, its expert) on entry
 // and its sorted row on exit.
+// tok_amax non-null (the forward that quantizes X inside FC1): each placed
+// row also gets its token's outer scale g = max|x| / 2688 in row_g.
 __global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restrict__ ids,
                                                           const float* __restrict__ probs, int64_t P, int32_t K,
                                                           int32_t E, int32_t capacity, const int32_t* __restrict__ blk_base,
                                                           const int32_t* __restrict__ expert_off, int32_t* pair2row,
-                                                          int32_t* __restrict__ row2pair, float* __restrict__ row_prob) {
+                                                          int32_t* __restrict__ row2pair, float* __restrict__ row_prob,
+                                                          const float* __restrict__ tok_amax, float* __restrict__ row_g) {
     const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= P) return;
     const int32_t e = ids[p];
@@ -455,6 +471,7 @@ __global__ void __launch_bounds__(256) route_place_kernel(const int32_t* __restr
     pair2row[p] = row;
     row2pair[row] = (int32_t)p;
     row_prob[row] = probs[p];
+    if (tok_amax) row_g[row] = row_scale(tok_amax[(uint32_t)p / (uint32_t)K]).g;
 }
 
 constexpr int kGatherSteps = 2;  // 128-column steps per gather wave (one 128-byte line of a row's codes)
@@ -529,10 +546,11 @@ __global__ void __launch_bounds__(256) route_gather_kernel(int32_t H, int32_t K,
 
 hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* probs, int32_t T, int32_t H, int32_t K,
                         int32_t E, int32_t capacity, bool round_up, const RouteBuffers& rb, int64_t rows_cap,
-                        hipStream_t stream, bool quant_x) {
+                        hipStream_t stream, bool quant_x, bool online) {
     const int64_t P = (int64_t)T * K;
     hipError_t st;
-    if (P <= kSmallPairs && T <= kSmallTokens && E <= kSmallExperts) {
+    if (online) quant_x = false;  // X is quantized inside FC1; the sort records each token's max |x|
+    if (!online && P <= kSmallPairs && T <= kSmallTokens && E <= kSmallExperts) {
         // workgroup 0 sorts; with X to quantize, workgroups 1.. take 8 rows each
         const unsigned qblocks = quant_x ? (unsigned)((T + kSmallWaves - 1) / kSmallWaves) : 0u;
         hipLaunchKernelGGL(route_small_kernel, dim3(1 + qblocks), dim3(kSmallWaves * 64), 0, stream, x, ids, probs, T,
@@ -541,9 +559,11 @@ hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* prob
         if (st != hipSuccess) return st;
     } else {
     const int32_t nblk = (T + kTokPerBlk - 1) / kTokPerBlk;
-    hipLaunchKernelGGL(quant_x ? route_count_kernel<true> : route_count_kernel<false>, dim3(nblk), dim3(kCountThreads),
-                       0, stream, x, ids, T, H, K, E, round_up ? 1 : 0, quant_x ? 1 : 0, rb.blk_counts, rb.blk_err,
-                       rb.pair2row /* holds the ranks until route_place */, rb.xq_codes, rb.xq_scales, rb.gx);
+    hipLaunchKernelGGL(online ? route_count_kernel<kXAmax> : quant_x ? route_count_kernel<kXQuant>
+                                                                     : route_count_kernel<kXNone>,
+                       dim3(nblk), dim3(kCountThreads), 0, stream, x, ids, T, H, K, E, round_up ? 1 : 0,
+                       quant_x ? 1 : 0, rb.blk_counts, rb.blk_err, rb.pair2row /* holds the ranks until route_place */,
+                       rb.xq_codes, rb.xq_scales, rb.gx);
     st = hipGetLastError();
     if (st != hipSuccess) return st;
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, nblk, E, capacity, rb.blk_counts, rb.blk_err,
@@ -552,7 +572,8 @@ hipError_t launch_route(const uint16_t* x, const int32_t* ids, const float* prob
     st = hipGetLastError();
     if (st != hipSuccess) return st;
     hipLaunchKernelGGL(route_place_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, stream, ids, probs, P, K, E,
-                       capacity, rb.blk_counts, rb.expert_off, rb.pair2row, rb.row2pair, rb.row_prob);
+                       capacity, rb.blk_counts, rb.expert_off, rb.pair2row, rb.row2pair, rb.row_prob,
+                       online ? rb.gx : nullptr, rb.a_g);
     st = hipGetLastError();
     if (st != hipSuccess) return st;
     }

@@ -85,31 +85,32 @@ def test_forward_host_validation(m):
     W1 = m.QTensor(0x1000, 0x1000, 0x1000, E, 2 * I, H, m.LAYOUT_GEMM)
     W2 = m.QTensor(0x1000, 0x1000, 0x1000, E, H, I, m.LAYOUT_GEMM)
     need = m.workspace_bytes(cfg)
-    f = lib.nvfp4moe_moe_expert_forward
-    # null config / weights / workspace
-    assert f(None, fake, 1, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake, fake, need, None) == 1
-    assert f(ctypes.byref(cfg), fake, 1, fake, fake, None, ctypes.byref(W2), fake, fake, need, None) == 1
-    assert f(ctypes.byref(cfg), fake, 1, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake, None, need, None) == 1
-    # capacity and negative T
-    assert f(ctypes.byref(cfg), fake, 65, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake, fake, need, None) == 5
-    assert f(ctypes.byref(cfg), fake, -1, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake, fake, need, None) == 2
-    # undersized workspace
-    assert f(ctypes.byref(cfg), fake, 1, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake, fake, need - 1,
-             None) == 4
-    # weight tensor of the wrong shape or layout
-    bad = m.QTensor(0x1000, 0x1000, 0x1000, E, I, H, m.LAYOUT_GEMM)
-    assert f(ctypes.byref(cfg), fake, 1, fake, fake, ctypes.byref(bad), ctypes.byref(W2), fake, fake, need, None) == 2
-    bad = m.QTensor(0x1000, 0x1000, 0x1000, E, 2 * I, H, m.LAYOUT_LOGICAL)
-    assert f(ctypes.byref(cfg), fake, 1, fake, fake, ctypes.byref(bad), ctypes.byref(W2), fake, fake, need, None) == 2
-    # misaligned workspace and activations
-    assert f(ctypes.byref(cfg), fake, 1, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake,
-             ctypes.c_void_p(0x1010), need, None) == 3
-    assert f(ctypes.byref(cfg), ctypes.c_void_p(0x1002), 1, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake,
-             fake, need, None) == 3
-    # null activations with T > 0
-    assert f(ctypes.byref(cfg), None, 1, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake, fake, need, None) == 1
-    # T == 0 is a no-op that launches nothing
-    assert f(ctypes.byref(cfg), None, 0, None, None, ctypes.byref(W1), ctypes.byref(W2), None, fake, need, None) == 0
+    # the standard forward and the one that quantizes X inside FC1 share the checks
+    for f in (lib.nvfp4moe_moe_expert_forward, lib.nvfp4moe_moe_expert_forward_online):
+        # null config / weights / workspace
+        assert f(None, fake, 1, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake, fake, need, None) == 1
+        assert f(ctypes.byref(cfg), fake, 1, fake, fake, None, ctypes.byref(W2), fake, fake, need, None) == 1
+        assert f(ctypes.byref(cfg), fake, 1, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake, None, need, None) == 1
+        # capacity and negative T
+        assert f(ctypes.byref(cfg), fake, 65, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake, fake, need, None) == 5
+        assert f(ctypes.byref(cfg), fake, -1, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake, fake, need, None) == 2
+        # undersized workspace
+        assert f(ctypes.byref(cfg), fake, 1, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake, fake, need - 1,
+                 None) == 4
+        # weight tensor of the wrong shape or layout
+        bad = m.QTensor(0x1000, 0x1000, 0x1000, E, I, H, m.LAYOUT_GEMM)
+        assert f(ctypes.byref(cfg), fake, 1, fake, fake, ctypes.byref(bad), ctypes.byref(W2), fake, fake, need, None) == 2
+        bad = m.QTensor(0x1000, 0x1000, 0x1000, E, 2 * I, H, m.LAYOUT_LOGICAL)
+        assert f(ctypes.byref(cfg), fake, 1, fake, fake, ctypes.byref(bad), ctypes.byref(W2), fake, fake, need, None) == 2
+        # misaligned workspace and activations
+        assert f(ctypes.byref(cfg), fake, 1, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake,
+                 ctypes.c_void_p(0x1010), need, None) == 3
+        assert f(ctypes.byref(cfg), ctypes.c_void_p(0x1002), 1, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake,
+                 fake, need, None) == 3
+        # null activations with T > 0
+        assert f(ctypes.byref(cfg), None, 1, fake, fake, ctypes.byref(W1), ctypes.byref(W2), fake, fake, need, None) == 1
+        # T == 0 is a no-op that launches nothing
+        assert f(ctypes.byref(cfg), None, 0, None, None, ctypes.byref(W1), ctypes.byref(W2), None, fake, need, None) == 0
 
 
 def test_backward_host_validation(m):
