@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--cold-steps", type=int, default=50, help="extra forwards timed after a cache-evicting write")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-sized (T = 1, 8, 64) forwards")
     ap.add_argument("--no-w4a16", action="store_true", help="skip the W4A16 variant's forwards")
+    ap.add_argument("--no-online", action="store_true",
+                    help="skip the forward that quantizes X inside FC1 (secondary timing)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense NVFP4 linear")
     ap.add_argument("--no-skewed", action="store_true", help="skip the skewed-routing T = 16384 forwards")
     ap.add_argument("--no-router", action="store_true", help="skip the on-device router (scores + top-k)")
@@ -419,6 +421,24 @@ def main():
                "tflops": 2.0 * T * K * 3 * H * I / (w16_ms / 1e3) / 1e12,
                "what": "NVFP4 weights x BF16 activations (bf16 MFMA), same routing, producer and combine"}
 
+    # The forward with X's max, quantization and FC1 fused (secondary): the
+    # same workload and output bits, X quantized inside FC1 instead of by the
+    # sort and the gather.
+    online = None
+    if not args.no_online:
+        for _ in range(20):
+            m.moe_expert_forward_online(cfg, x, ids, probs, qw, ws, out=out)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(50):
+            m.moe_expert_forward_online(cfg, x, ids, probs, qw, ws, out=out, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        on_ms = ev[0].elapsed_time(ev[1]) / 50
+        online = {"ms_per_step": on_ms, "tokens_per_s": T / (on_ms / 1e3),
+                  "what": "X's max in the sort, its quantization inside FC1 (no quantized copy of X, no gather); "
+                          "outputs bitwise those of the headline forward"}
+
     # The BF16 straight-through backward (secondary): after the unfused forward
     # that stores y1, the backward of the same layer with a random upstream
     # gradient; dh, each pair's FC1 input gradient and both weight gradients
@@ -566,6 +586,8 @@ def main():
         result["backward"] = backward
     if w16:
         result["w4a16"] = w16
+    if online:
+        result["online_fc1_quant"] = online
     if dense:
         result["dense_linear"] = dense
     if skewed:
