@@ -126,10 +126,14 @@ def test_routing_edge_cases(gpu, orc):
     W.MoEShape(T=70, H=640, E=6, K=3, I=256),   # 5 K steps in FC1, 2 in FC2; FC2 N = 640
     W.MoEShape(T=450, H=256, E=3, K=2, I=640),  # about 300 rows per expert: 3 row tiles each, the
                                                 # last partial; I = 640: 5 FC1 column tiles, 5 FC2 K steps
+    W.MoEShape(T=40, H=4224, E=4, K=2, I=128),  # the sort's quantizer holds 3 groups per lane (idle lanes in
+                                                # the last); 33 FC1 K steps; FC2 N = 4224: a half column tile
+    W.MoEShape(T=24, H=8320, E=3, K=2, I=128),  # rows wider than 8192 columns: the quantizer's wave loop
 ])
 def test_unusual_shapes_all_stages(gpu, orc, shape):
-    """Layer shapes away from the workloads: K-step counts of 1, 2, 3, 5; column
-    tiles with idle waves; a single expert; K = E; several row tiles per expert."""
+    """Layer shapes away from the workloads: K-step counts of 1, 2, 3, 5, 33, 65;
+    column tiles with idle waves; a single expert; K = E; several row tiles per
+    expert; token rows too wide for the quantizer's registers."""
     m, dev = gpu
     wl = W.MoEWorkload(f"shape_H{shape.H}_I{shape.I}_E{shape.E}_K{shape.K}", 12, shape)
     layer = Layer(m, dev, wl, max_tokens=shape.T)

@@ -9,7 +9,9 @@ row itself.  Every quantized group must come out as the standard quantizer
 made it, so FC1's output h (with its per-32-column maxima), FC2's input and
 output and the layer output must be the standard forward's bit for bit --
 on the tiny layer in both scale roundings, odd shapes (K = E, a partial
-column tile, one expert), the Qwen3-shaped layer at T = 4096 and Zipf-skewed
+column tile, one expert, token rows of 4224 and 8320 columns, which the
+sort's max takes in registers and in its wave loop), the Qwen3-shaped layer
+at T = 4096 and Zipf-skewed
 routing at T = 16384 -- and the standard forward is itself compared element
 by element with the oracle (tests/test_gpu_layer.py).  Each token's output
 is also bitwise the same alone as in its batch."""
@@ -74,7 +76,9 @@ def test_online_equals_standard_tiny(gpu, mode):
 
 @pytest.mark.parametrize("shape", [W.MoEShape(T=37, H=384, E=5, K=5, I=384),    # every token to every expert
                                    W.MoEShape(T=450, H=256, E=3, K=2, I=640),   # a partial FC1 column tile
-                                   W.MoEShape(T=200, H=128, E=1, K=1, I=128)])  # one expert
+                                   W.MoEShape(T=200, H=128, E=1, K=1, I=128),   # one expert
+                                   W.MoEShape(T=40, H=4224, E=4, K=2, I=128),    # 3 register groups per lane
+                                   W.MoEShape(T=24, H=8320, E=3, K=2, I=128)])   # the sort's wave loop
 def test_online_equals_standard_odd_shapes(gpu, shape):
     m, dev = gpu
     _compare(m, dev, W.MoEWorkload("odd", 12, shape))
