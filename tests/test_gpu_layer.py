@@ -129,6 +129,8 @@ def test_routing_edge_cases(gpu, orc):
     W.MoEShape(T=40, H=4224, E=4, K=2, I=128),  # the sort's quantizer holds 3 groups per lane (idle lanes in
                                                 # the last); 33 FC1 K steps; FC2 N = 4224: a half column tile
     W.MoEShape(T=24, H=8320, E=3, K=2, I=128),  # rows wider than 8192 columns: the quantizer's wave loop
+    W.MoEShape(T=150, H=4224, E=4, K=2, I=128),  # the same two widths past 128 tokens, where the block-wise
+    W.MoEShape(T=150, H=8320, E=3, K=2, I=128),  # sort (not the single-launch one) quantizes X
 ])
 def test_unusual_shapes_all_stages(gpu, orc, shape):
     """Layer shapes away from the workloads: K-step counts of 1, 2, 3, 5, 33, 65;
