@@ -323,7 +323,7 @@ int forward_impl(const nvfp4moe_config* cfg, const uint16_t* x, int32_t T, const
         g1.K = (int32_t)H;
         g1.N = (int32_t)(2 * I);
         g1.n_tiles_n = col_tiles(I, kGemmSwiGLU);
-        g1.mtiles = rb.mtiles;
+        g1.mtiles = rb.mtiles_even;  // each expert's subtiles spread evenly over its row tiles (as the W4A4 FC1)
         g1.n_mtiles = rb.n_mtiles;
         g1.out = (uint16_t*)(ws + L.pub.h);
         g1.ld_out = I;

@@ -236,13 +236,22 @@ __device__ __forceinline__ void w16_tile(const W16Params& P, W16SharedA& S, int3
 // One workgroup of 4 waves per (row tile of up to 128 rows, column tile):
 // the activation tile is loaded once per 128-column step (wave w loads
 // subtile w) into LDS, from where every wave reads its MFMA operands; each
-// wave decodes its own weight columns in registers.
+// wave decodes its own weight columns in registers.  Workgroup b runs on XCD
+// b % 8 (round-robin dispatch), and XCD x takes the contiguous range
+// [x * span, (x + 1) * span) of the device's tile list, so a row tile's
+// column tiles and an expert's row tiles -- which share activations and a
+// weight slab -- meet in one XCD's L2.  The grid (a multiple of 8) covers
+// the static tile bound.
 template <int MODE>
 __global__ void __launch_bounds__(256, 2) gemm_w4a16_kernel(W16Params P) {
     __shared__ W16SharedA S;
-    const int32_t nt = (int32_t)(blockIdx.x % P.n_tiles_n);
-    const int64_t mt = blockIdx.x / P.n_tiles_n;
-    if (mt >= *P.n_mtiles) return;
+    const int64_t total = (int64_t)(*P.n_mtiles) * P.n_tiles_n;
+    const int64_t span = (total + 7) / 8, slot = blockIdx.x >> 3;
+    if (slot >= span) return;
+    const int64_t tile = (int64_t)(blockIdx.x & 7) * span + slot;
+    if (tile >= total) return;
+    const int32_t nt = (int32_t)(tile % P.n_tiles_n);
+    const int64_t mt = tile / P.n_tiles_n;
     const int4 d = P.mtiles[mt];
     switch (d.z) {
         case 4: w16_tile<MODE, 4>(P, S, d.x, d.y, d.w, nt); break;
@@ -253,7 +262,7 @@ __global__ void __launch_bounds__(256, 2) gemm_w4a16_kernel(W16Params P) {
 }
 
 hipError_t launch_gemm_w4a16(int mode, const W16Params& P, int64_t mt_bound, hipStream_t stream) {
-    const int64_t blocks = mt_bound * P.n_tiles_n;
+    const int64_t blocks = (mt_bound * P.n_tiles_n + 7) / 8 * 8;
     if (blocks <= 0) return hipSuccess;
     if (mode == kGemmSwiGLU)
         hipLaunchKernelGGL(gemm_w4a16_kernel<kGemmSwiGLU>, dim3((unsigned)blocks), dim3(256), 0, stream, P);
