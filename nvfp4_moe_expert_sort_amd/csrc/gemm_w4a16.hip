@@ -81,6 +81,10 @@ __device__ __forceinline__ void w16_tile(const W16Params& P, W16SharedA& S, int3
     // them) and reads wave 0's weight columns, which it never uses.
     const int32_t wcol = active ? 0 : (MODE == kGemmSwiGLU ? 32 : 64) * wave;
     const int r = lane & 31, h = lane >> 5;
+    // The weight global scales of this wave's columns (column r of each
+    // column tile), for the epilogue, loaded before the K loop.
+    const int64_t wrow0 = (int64_t)expert * P.N;
+    const float cg0 = P.b_g[wrow0 + bcol[0] - wcol + r], cg1 = P.b_g[wrow0 + bcol[1] - wcol + r];
     const int64_t K = P.K, kc64 = K >> 6, kc128 = K >> 7;
     // activation row of this wave's subtile (a wave past the tile's subtiles
     // re-reads subtile 0 and stores nothing)
@@ -180,10 +184,9 @@ __device__ __forceinline__ void w16_tile(const W16Params& P, W16SharedA& S, int3
     // accesses complete in order.
     constexpr int kPitch = 72;  // halves per staged row: 64 columns + 8 pad
     uint16_t* E = reinterpret_cast<uint16_t*>(&S) + wave * (32 * kPitch);
-    const int64_t wrow0 = (int64_t)expert * P.N;
     const int rowL = h * 4;
     if (MODE == kGemmSwiGLU) {
-        const float gg = P.b_g[wrow0 + bcol[0] + r], gu = P.b_g[wrow0 + bcol[1] + r];
+        const float gg = cg0, gu = cg1;
 #pragma unroll
         for (int t = 0; t < NSUB; t++) {
 #pragma unroll
@@ -208,7 +211,7 @@ __device__ __forceinline__ void w16_tile(const W16Params& P, W16SharedA& S, int3
             __builtin_amdgcn_wave_barrier();
         }
     } else {
-        const float g0 = P.b_g[wrow0 + bcol[0] + r], g1 = P.b_g[wrow0 + bcol[1] + r];
+        const float g0 = cg0, g1 = cg1;
 #pragma unroll
         for (int t = 0; t < NSUB; t++) {
 #pragma unroll
