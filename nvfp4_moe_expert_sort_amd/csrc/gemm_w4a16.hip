@@ -186,6 +186,13 @@ __device__ __forceinline__ void w16_tile(const W16Params& P, W16SharedA& S, int3
     uint16_t* E = reinterpret_cast<uint16_t*>(&S) + wave * (32 * kPitch);
     const int rowL = h * 4;
     if (MODE == kGemmSwiGLU) {
+        // h leaves in whole 128-byte lines: each wave stages its 32 columns of
+        // all the tile's rows, then the workgroup stores the tile's 128 columns
+        // (256 bytes of each row), 16 lanes per row.  (All four waves get
+        // here: the inner size is a multiple of 128, so every wave has h
+        // columns.)
+        constexpr int kPitchH = 40;  // halves per staged row: 32 columns + 8 pad (80 B, conflict-free)
+        uint16_t* EH = reinterpret_cast<uint16_t*>(&S) + wave * (128 * kPitchH);
         const float gg = cg0, gu = cg1;
 #pragma unroll
         for (int t = 0; t < NSUB; t++) {
@@ -195,20 +202,23 @@ __device__ __forceinline__ void w16_tile(const W16Params& P, W16SharedA& S, int3
                 const int32_t row = min(row0 + 32 * t + rr, row_end - 1);  // rows past the end are not stored
                 const float yg = __uint_as_float(bf16_hw(acc[t][0][i] * gg) << 16);
                 const float yu = __uint_as_float(bf16_hw(acc[t][1][i] * gu) << 16);
-                E[rr * kPitch + r] = (uint16_t)swiglu_prob_bf16(yg, yu, P.row_prob[row]);
+                EH[(32 * t + rr) * kPitchH + r] = (uint16_t)swiglu_prob_bf16(yg, yu, P.row_prob[row]);
             }
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slice is written
-            __builtin_amdgcn_wave_barrier();
-            // lane l: row l % 32, columns 16 (l / 32) .. + 16 of the wave's 32 h columns
-            const int32_t row = row0 + 32 * t + r;
-            if (row < row_end) {
-                const u32x4* src = reinterpret_cast<const u32x4*>(E + r * kPitch + 16 * h);
-                u32x4* dst = reinterpret_cast<u32x4*>(P.out + (int64_t)row * P.ld_out + bcol[0] + 16 * h);
-                dst[0] = src[0];
-                dst[1] = src[1];
-            }
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // read before the next pass overwrites the slice
-            __builtin_amdgcn_wave_barrier();
+        }
+        w16_barrier_lds();
+        // (the thread index passes through an empty asm after the barrier, so
+        // the store addresses are not computed early and held in registers)
+        int tid = (int)threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const uint16_t* E0 = reinterpret_cast<const uint16_t*>(&S);
+        const int32_t hc0 = bcol[0] - 32 * wave;  // the tile's first h column
+#pragma unroll
+        for (int q = 0; q < 2 * NSUB; q++) {
+            const int c = q * 256 + tid;
+            const int rl = c >> 4, cc = c & 15;  // row of the tile, 8-column chunk (wave cc / 4's slice)
+            const u32x4 v = *reinterpret_cast<const u32x4*>(E0 + (cc >> 2) * (128 * kPitchH) + rl * kPitchH + 8 * (cc & 3));
+            const int32_t row = row0 + rl;
+            if (row < row_end) *reinterpret_cast<u32x4*>(P.out + (int64_t)row * P.ld_out + hc0 + 8 * cc) = v;
         }
     } else {
         const float g0 = cg0, g1 = cg1;
